@@ -1,0 +1,192 @@
+"""ctypes binding of libpi_ffn.so (the C ABI declared in include/pi_ffn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  PyTorch supplies device memory and streams.  If the
+library is not built, importing this module raises ImportError: there is no
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PI_FFN_LIB", os.path.join(PKG_DIR, "libpi_ffn.so"))
+
+PI_OK, PI_ERR_INVALID, PI_ERR_WORKSPACE, PI_ERR_HIP, PI_ERR_UNSUPPORTED = range(5)
+PI_F32, PI_F16, PI_Q4G32 = range(3)
+PI_MASK_PREDICTED, PI_MASK_EXACT_RELU, PI_MASK_DENSE = range(3)
+(PI_PHASE_PRED_HIDDEN, PI_PHASE_PRED_MASK, PI_PHASE_DENSE_PRE, PI_PHASE_GATHER,
+ PI_PHASE_DOWN, PI_PHASE_COUNT) = range(6)
+
+DTYPES = {"f32": PI_F32, "f16": PI_F16, "q4g32": PI_Q4G32}
+MODES = {"predicted": PI_MASK_PREDICTED, "exact": PI_MASK_EXACT_RELU, "dense": PI_MASK_DENSE}
+PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "pred_mask": PI_PHASE_PRED_MASK,
+          "dense_pre": PI_PHASE_DENSE_PRE, "gather": PI_PHASE_GATHER, "down": PI_PHASE_DOWN}
+STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_ERR_HIP", 4: "PI_ERR_UNSUPPORTED"}
+
+EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",
+            "pi_ffn_destroy", "pi_ffn_predict", "pi_ffn_forward", "pi_ffn_forward_masked",
+            "pi_ffn_profile_next")
+
+
+class PiDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ffn", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("gated", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+                ("p_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("tau", ctypes.c_float)]
+
+
+class PiWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("w_gate", "w_up", "w_down_t", "s_gate", "s_up", "s_down", "b", "p1", "p2", "b_p")]
+
+
+class PiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "or `python activation_sparse_decode_relu_amd/_build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+    lib.pi_ffn_abi_version.restype = i32
+    lib.pi_ffn_abi_version.argtypes = []
+    lib.pi_last_error.restype = ctypes.c_char_p
+    lib.pi_last_error.argtypes = []
+    lib.pi_ffn_workspace_bytes.restype = st
+    lib.pi_ffn_workspace_bytes.argtypes = [ctypes.POINTER(PiDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.pi_ffn_create.restype = st
+    lib.pi_ffn_create.argtypes = [ctypes.POINTER(PiDesc), ctypes.POINTER(PiWeights), vp, ctypes.c_size_t, vp,
+                                  ctypes.POINTER(vp)]
+    lib.pi_ffn_destroy.restype = st
+    lib.pi_ffn_destroy.argtypes = [vp]
+    lib.pi_ffn_predict.restype = st
+    lib.pi_ffn_predict.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.pi_ffn_forward.restype = st
+    lib.pi_ffn_forward.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
+    lib.pi_ffn_forward_masked.restype = st
+    lib.pi_ffn_forward_masked.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.pi_ffn_profile_next.restype = st
+    lib.pi_ffn_profile_next.argtypes = [vp, i32, vp, vp]
+    return lib
+
+
+LIB = _load()
+
+
+def last_error() -> str:
+    return LIB.pi_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != PI_OK:
+        raise PiError(status, last_error())
+
+
+def make_desc(d_model, d_ffn, rank, gated, max_batch, w_dtype, p_dtype, act_dtype, tau=0.5) -> PiDesc:
+    def dt(v):
+        return DTYPES[v] if isinstance(v, str) else int(v)
+    return PiDesc(int(d_model), int(d_ffn), int(rank), int(bool(gated)), int(max_batch), dt(w_dtype),
+                  dt(p_dtype), dt(act_dtype), float(tau))
+
+
+def workspace_bytes(desc: PiDesc) -> int:
+    out = ctypes.c_size_t(0)
+    check(LIB.pi_ffn_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) or None
+
+
+class FFNLayer:
+    """One layer bound to device tensors: a handle of the C library.
+
+    `tensors` maps w_gate, w_up, w_down_t, s_gate, s_up, s_down, b, p1, p2, b_p
+    to CUDA tensors (or None).  The layer keeps references to them and to its
+    workspace for as long as the handle lives.
+    """
+
+    def __init__(self, desc: PiDesc, tensors: dict, workspace=None, stream=None):
+        import torch
+        self.desc = desc
+        self.tensors = dict(tensors)
+        need = workspace_bytes(desc)
+        if workspace is None:
+            dev = next(t.device for t in self.tensors.values() if t is not None)
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        w = PiWeights(*[_ptr(self.tensors.get(k)) for k, _ in PiWeights._fields_])
+        handle = ctypes.c_void_p()
+        check(LIB.pi_ffn_create(ctypes.byref(desc), ctypes.byref(w), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream),
+                                ctypes.byref(handle)))
+        self.handle = handle
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            check(LIB.pi_ffn_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def predict(self, x, idx, count, logits_dbg=None, stream=None) -> None:
+        check(LIB.pi_ffn_predict(self.handle, _ptr(x), int(x.shape[0]), _ptr(idx), _ptr(count),
+                                 _ptr(logits_dbg), _stream(stream)))
+
+    def forward(self, x, y, mode="predicted", idx_out=None, count_out=None, stream=None) -> None:
+        m = MODES[mode] if isinstance(mode, str) else int(mode)
+        check(LIB.pi_ffn_forward(self.handle, _ptr(x), int(x.shape[0]), m, _ptr(y), _ptr(idx_out),
+                                 _ptr(count_out), _stream(stream)))
+
+    def forward_masked(self, x, idx, count, y, stream=None) -> None:
+        check(LIB.pi_ffn_forward_masked(self.handle, _ptr(x), int(x.shape[0]), _ptr(idx), _ptr(count),
+                                        _ptr(y), _stream(stream)))
+
+    def profile_next(self, phase, start_event, stop_event) -> None:
+        p = PHASES[phase] if isinstance(phase, str) else int(phase)
+        s0 = None if start_event is None else int(start_event.cuda_event)
+        s1 = None if stop_event is None else int(stop_event.cuda_event)
+        check(LIB.pi_ffn_profile_next(self.handle, p, s0, s1))
+
+
+_TENSOR_NAMES = ("w_gate", "w_up", "w_down_t", "s_gate", "s_up", "s_down", "b", "p1", "p2", "b_p")
+
+
+def upload_layer(layer, device="cuda", max_batch=1, workspace=None, stream=None,
+                 with_predictor=True) -> FFNLayer:
+    """Copy a host layer (numpy arrays, neuron-major) to `device` and bind a handle."""
+    import torch
+    tensors = {}
+    for name in _TENSOR_NAMES:
+        arr = getattr(layer, name, None)
+        if arr is None or (not with_predictor and name in ("p1", "p2", "b_p")):
+            tensors[name] = None
+            continue
+        tensors[name] = torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    rank = layer.rank if (with_predictor and layer.p1 is not None) else 0
+    desc = make_desc(layer.d_model, layer.d_ffn, rank, layer.gated, max_batch, layer.w_dtype,
+                     layer.p_dtype, layer.act_dtype, layer.tau)
+    return FFNLayer(desc, tensors, workspace=workspace, stream=stream)

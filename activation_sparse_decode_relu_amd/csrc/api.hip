@@ -1,0 +1,341 @@
+// C ABI of the activation-sparse ReLU FFN decode library: argument checks,
+// workspace layout and the kernel sequence of each call.
+//
+// Sequences (PowerInfer paper explainer, section "GPU-CPUハイブリッドアーキテクチャ",
+// inference flow: predict, then compute only the predicted neurons):
+//   predict            pred_hidden -> rows_mask(P2, h)             -> idx, count
+//   forward PREDICTED  pred_hidden -> rows_mask(P2, h) -> gather -> down
+//   forward EXACT      rows_mask(W_gate|W_up, x) -> [gather(up only)] -> down
+//   forward DENSE      gather(all neurons) -> down(all neurons)
+//   forward_masked     gather(caller list) -> down(caller list)
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "kernels.h"
+#include "pi_ffn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pi_status fail(pi_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pi_status ok() {
+  g_last_error.clear();
+  return PI_OK;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxBatch = 16;
+constexpr int kMaxSplits = 64;       // neuron slices of the down projection
+constexpr int kDownTargetWG = 256;   // workgroups the down projection aims for
+constexpr int kGatherMaxWG = 1024;   // persistent gather grid cap (4 waves each)
+constexpr int kMaxD = 1 << 20;
+constexpr int kMaxN = 1 << 24;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t tickets, h, mask, idx, count, g, a, partial, total;
+  int n_tickets, n_tiles, splits;
+};
+
+Layout layout_for(const pi_ffn_desc& d) {
+  Layout L{};
+  const size_t B = (size_t)d.max_batch, n = (size_t)d.d_ffn, dm = (size_t)d.d_model;
+  const int tw = pik::down_tile_width(d.w_dtype);
+  L.n_tiles = (d.d_model + tw - 1) / tw;
+  int s = kDownTargetWG / L.n_tiles;
+  L.splits = s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+  L.n_tickets = 2 + L.n_tiles;  // [0] predictor mask, [1] dense pre-activation, [2..] down tiles
+  size_t off = 0;
+  L.tickets = off; off = align_up(off + sizeof(unsigned) * L.n_tickets);
+  L.h = off;       off = align_up(off + sizeof(float) * B * (size_t)(d.rank > 0 ? d.rank : 1));
+  L.mask = off;    off = align_up(off + sizeof(unsigned long long) * ((n + 63) / 64));
+  L.idx = off;     off = align_up(off + sizeof(int) * n);
+  L.count = off;   off = align_up(off + sizeof(int));
+  L.g = off;       off = align_up(off + sizeof(float) * B * n);
+  L.a = off;       off = align_up(off + sizeof(float) * B * n);
+  L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.splits * B * dm);
+  L.total = off;
+  return L;
+}
+
+pi_status check_desc(const pi_ffn_desc* d) {
+  if (d == nullptr) return fail(PI_ERR_INVALID, "desc is NULL");
+  if (d->d_model <= 0 || d->d_model % 64 != 0 || d->d_model > kMaxD)
+    return fail(PI_ERR_INVALID, "d_model=%d must be a positive multiple of 64 up to %d", d->d_model, kMaxD);
+  if (d->d_ffn <= 0 || d->d_ffn > kMaxN)
+    return fail(PI_ERR_INVALID, "d_ffn=%d must lie in [1, %d]", d->d_ffn, kMaxN);
+  if (d->rank < 0 || d->rank % 64 != 0 || d->rank > kMaxD)
+    return fail(PI_ERR_INVALID, "rank=%d must be 0 or a positive multiple of 64", d->rank);
+  if (d->gated != 0 && d->gated != 1) return fail(PI_ERR_INVALID, "gated=%d must be 0 or 1", d->gated);
+  if (d->max_batch < 1 || d->max_batch > kMaxBatch)
+    return fail(PI_ERR_INVALID, "max_batch=%d must lie in [1, %d]", d->max_batch, kMaxBatch);
+  if (d->w_dtype != PI_F32 && d->w_dtype != PI_F16 && d->w_dtype != PI_Q4G32)
+    return fail(PI_ERR_INVALID, "w_dtype=%d is not a pi_dtype", d->w_dtype);
+  if (d->p_dtype != PI_F32 && d->p_dtype != PI_F16)
+    return fail(PI_ERR_INVALID, "p_dtype=%d must be PI_F32 or PI_F16", d->p_dtype);
+  if (d->act_dtype != PI_F32 && d->act_dtype != PI_F16)
+    return fail(PI_ERR_INVALID, "act_dtype=%d must be PI_F32 or PI_F16", d->act_dtype);
+  if (d->rank > 0 && !(d->tau > 0.0f && d->tau < 1.0f))
+    return fail(PI_ERR_INVALID, "tau=%g must lie in (0, 1)", (double)d->tau);
+  return PI_OK;
+}
+
+pi_status check_weights(const pi_ffn_desc* d, const pi_ffn_weights* w) {
+  if (w == nullptr) return fail(PI_ERR_INVALID, "weights is NULL");
+  const bool q4 = d->w_dtype == PI_Q4G32;
+  struct Req { const void* p; bool need; const char* name; };
+  const Req reqs[] = {
+      {w->w_gate, d->gated == 1, "w_gate"}, {w->w_up, true, "w_up"},       {w->w_down_t, true, "w_down_t"},
+      {w->s_gate, q4 && d->gated == 1, "s_gate"}, {w->s_up, q4, "s_up"},    {w->s_down, q4, "s_down"},
+      {w->b, true, "b"},                      {w->p1, d->rank > 0, "p1"},   {w->p2, d->rank > 0, "p2"},
+      {w->b_p, d->rank > 0, "b_p"},
+  };
+  for (const Req& r : reqs) {
+    if (r.need && r.p == nullptr) return fail(PI_ERR_INVALID, "%s is NULL but required by the descriptor", r.name);
+    if (!r.need && r.p != nullptr) return fail(PI_ERR_INVALID, "%s must be NULL for this descriptor", r.name);
+    if (r.p != nullptr && !aligned16(r.p)) return fail(PI_ERR_INVALID, "%s is not 16-byte aligned", r.name);
+  }
+  return PI_OK;
+}
+
+}  // namespace
+
+struct pi_ffn {
+  pi_ffn_desc desc;
+  pi_ffn_weights w;
+  char* ws;
+  size_t ws_bytes;
+  Layout L;
+  float thr;
+  int gather_grid;
+  void* prof_start[PI_PHASE_COUNT];
+  void* prof_stop[PI_PHASE_COUNT];
+
+  unsigned* tickets() const { return reinterpret_cast<unsigned*>(ws + L.tickets); }
+  float* h() const { return reinterpret_cast<float*>(ws + L.h); }
+  unsigned long long* mask() const { return reinterpret_cast<unsigned long long*>(ws + L.mask); }
+  int* idx() const { return reinterpret_cast<int*>(ws + L.idx); }
+  int* count() const { return reinterpret_cast<int*>(ws + L.count); }
+  float* g() const { return reinterpret_cast<float*>(ws + L.g); }
+  float* a() const { return reinterpret_cast<float*>(ws + L.a); }
+  float* partial() const { return reinterpret_cast<float*>(ws + L.partial); }
+};
+
+namespace {
+
+// Launch one phase, bracketed by the armed profiling events if any.
+template <typename F>
+pi_status run_phase(pi_ffn* h, int phase, hipStream_t s, const char* what, F&& launch) {
+  void* ev0 = h->prof_start[phase];
+  void* ev1 = h->prof_stop[phase];
+  if (ev0 != nullptr) {
+    h->prof_start[phase] = h->prof_stop[phase] = nullptr;
+    if (hipEventRecord(static_cast<hipEvent_t>(ev0), s) != hipSuccess)
+      return fail(PI_ERR_HIP, "hipEventRecord before %s failed", what);
+  }
+  const hipError_t e = launch();
+  if (e != hipSuccess) return fail(PI_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  if (ev1 != nullptr && hipEventRecord(static_cast<hipEvent_t>(ev1), s) != hipSuccess)
+    return fail(PI_ERR_HIP, "hipEventRecord after %s failed", what);
+  return PI_OK;
+}
+
+pi_status check_call(pi_ffn* h, const void* x, int32_t batch, const void* y, bool need_y) {
+  if (h == nullptr) return fail(PI_ERR_INVALID, "handle is NULL");
+  if (batch < 1 || batch > h->desc.max_batch)
+    return fail(PI_ERR_INVALID, "batch=%d must lie in [1, max_batch=%d]", batch, h->desc.max_batch);
+  if (x == nullptr || !aligned16(x)) return fail(PI_ERR_INVALID, "x is NULL or not 16-byte aligned");
+  if (need_y && (y == nullptr || !aligned16(y))) return fail(PI_ERR_INVALID, "y is NULL or not 16-byte aligned");
+  return PI_OK;
+}
+
+pi_status check_opt_ptr(const void* p, const char* name) {
+  if (p != nullptr && !aligned16(p)) return fail(PI_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return PI_OK;
+}
+
+// Predictor mask: h = ReLU(x P1^T), then logits, threshold, ballot, compaction.
+pi_status predictor_phases(pi_ffn* h, const void* x, int B, int* idx, int* count, float* logits, hipStream_t s) {
+  const pi_ffn_desc& d = h->desc;
+  pi_status st = run_phase(h, PI_PHASE_PRED_HIDDEN, s, "pred_hidden", [&] {
+    return pik::launch_pred_hidden(d.p_dtype, d.act_dtype, h->w.p1, x, d.d_model, d.rank, B, h->h(), s);
+  });
+  if (st != PI_OK) return st;
+  return run_phase(h, PI_PHASE_PRED_MASK, s, "pred_mask", [&] {
+    return pik::launch_rows_mask(d.p_dtype, PI_F32, h->w.p2, nullptr, h->h(), d.rank, d.d_ffn, h->w.b_p, h->thr, B,
+                                 logits, h->mask(), h->tickets() + 0, idx, count, s);
+  });
+}
+
+pi_status sparse_phases(pi_ffn* h, const void* x, int B, int gm, int asrc, bool gather, const int* idx,
+                        const int* count, int dense, int* iota_out, int* count_out, void* y, hipStream_t s) {
+  const pi_ffn_desc& d = h->desc;
+  if (gather) {
+    pi_status st = run_phase(h, PI_PHASE_GATHER, s, "gather", [&] {
+      return pik::launch_gather(d.w_dtype, d.act_dtype, gm, h->w.w_gate, h->w.w_up, h->w.s_gate, h->w.s_up, h->w.b,
+                                h->g(), x, d.d_model, d.d_ffn, B, idx, count, dense, h->a(), iota_out, count_out,
+                                h->gather_grid, s);
+    });
+    if (st != PI_OK) return st;
+  }
+  return run_phase(h, PI_PHASE_DOWN, s, "down", [&] {
+    return pik::launch_down(d.w_dtype, d.act_dtype, asrc, h->w.w_down_t, h->w.s_down, h->a(), h->g(), d.d_model,
+                            d.d_ffn, B, idx, count, dense, h->L.splits, h->partial(), h->tickets() + 2, y, s);
+  });
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pi_ffn_abi_version(void) { return PI_FFN_ABI_VERSION; }
+
+const char* pi_last_error(void) { return g_last_error.c_str(); }
+
+pi_status pi_ffn_workspace_bytes(const pi_ffn_desc* desc, size_t* bytes) {
+  pi_status st = check_desc(desc);
+  if (st != PI_OK) return st;
+  if (bytes == nullptr) return fail(PI_ERR_INVALID, "bytes is NULL");
+  *bytes = layout_for(*desc).total;
+  return ok();
+}
+
+pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights, void* workspace,
+                        size_t workspace_bytes, void* stream, pi_ffn** out) {
+  if (out == nullptr) return fail(PI_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  pi_status st = check_desc(desc);
+  if (st != PI_OK) return st;
+  if ((st = check_weights(desc, weights)) != PI_OK) return st;
+  const Layout L = layout_for(*desc);
+  if (workspace == nullptr) return fail(PI_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(PI_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(PI_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  pi_ffn* h = new (std::nothrow) pi_ffn{};
+  if (h == nullptr) return fail(PI_ERR_INVALID, "out of host memory");
+  h->desc = *desc;
+  h->w = *weights;
+  h->ws = static_cast<char*>(workspace);
+  h->ws_bytes = workspace_bytes;
+  h->L = L;
+  h->thr = desc->rank > 0 ? (float)std::log((double)desc->tau / (1.0 - (double)desc->tau)) : 0.0f;
+  const int want = (desc->d_ffn + 3) / 4;
+  h->gather_grid = want < kGatherMaxWG ? want : kGatherMaxWG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pik::launch_fill_u32(h->tickets(), L.n_tickets, 0u, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(PI_ERR_HIP, "workspace initialisation failed: %s", hipGetErrorString(e));
+  }
+  *out = h;
+  return ok();
+}
+
+pi_status pi_ffn_destroy(pi_ffn* h) {
+  if (h == nullptr) return fail(PI_ERR_INVALID, "handle is NULL");
+  delete h;
+  return ok();
+}
+
+pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, int32_t* count, float* logits_dbg,
+                         void* stream) {
+  pi_status st = check_call(h, x, batch, nullptr, false);
+  if (st != PI_OK) return st;
+  if (h->desc.rank == 0) return fail(PI_ERR_INVALID, "predict needs a predictor (rank > 0)");
+  if (idx == nullptr || count == nullptr) return fail(PI_ERR_INVALID, "idx and count are required");
+  if ((st = check_opt_ptr(idx, "idx")) != PI_OK || (st = check_opt_ptr(count, "count")) != PI_OK ||
+      (st = check_opt_ptr(logits_dbg, "logits_dbg")) != PI_OK)
+    return st;
+  st = predictor_phases(h, x, batch, idx, count, logits_dbg, static_cast<hipStream_t>(stream));
+  return st == PI_OK ? ok() : st;
+}
+
+pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
+                         int32_t* count_out, void* stream) {
+  pi_status st = check_call(h, x, batch, y, true);
+  if (st != PI_OK) return st;
+  if ((st = check_opt_ptr(idx_out, "idx_out")) != PI_OK || (st = check_opt_ptr(count_out, "count_out")) != PI_OK)
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const pi_ffn_desc& d = h->desc;
+  int* idx = idx_out != nullptr ? idx_out : h->idx();
+  int* count = count_out != nullptr ? count_out : h->count();
+  switch (mask_mode) {
+    case PI_MASK_PREDICTED:
+      if (d.rank == 0) return fail(PI_ERR_INVALID, "PREDICTED mode needs a predictor (rank > 0)");
+      st = predictor_phases(h, x, batch, idx, count, nullptr, s);
+      if (st == PI_OK)
+        st = sparse_phases(h, x, batch, d.gated ? pik::GM_GATED : pik::GM_NONGATED, pik::ASRC_A, true, idx, count,
+                           0, nullptr, nullptr, y, s);
+      break;
+    case PI_MASK_EXACT_RELU:
+      st = run_phase(h, PI_PHASE_DENSE_PRE, s, "dense_pre", [&] {
+        return pik::launch_rows_mask(d.w_dtype, d.act_dtype, d.gated ? h->w.w_gate : h->w.w_up,
+                                     d.gated ? h->w.s_gate : h->w.s_up, x, d.d_model, d.d_ffn, h->w.b, 0.0f, batch,
+                                     h->g(), h->mask(), h->tickets() + 1, idx, count, s);
+      });
+      if (st == PI_OK) {
+        if (d.gated)
+          st = sparse_phases(h, x, batch, pik::GM_EXACT_GATED, pik::ASRC_A, true, idx, count, 0, nullptr, nullptr, y,
+                             s);
+        else
+          st = sparse_phases(h, x, batch, pik::GM_NONGATED, pik::ASRC_GRELU, false, idx, count, 0, nullptr, nullptr,
+                             y, s);
+      }
+      break;
+    case PI_MASK_DENSE:
+      st = sparse_phases(h, x, batch, d.gated ? pik::GM_GATED : pik::GM_NONGATED, pik::ASRC_A, true, nullptr,
+                         nullptr, 1, idx_out, count_out, y, s);
+      break;
+    default:
+      return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
+  }
+  return st == PI_OK ? ok() : st;
+}
+
+pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx, const int32_t* count,
+                                void* y, void* stream) {
+  pi_status st = check_call(h, x, batch, y, true);
+  if (st != PI_OK) return st;
+  if (idx == nullptr || count == nullptr) return fail(PI_ERR_INVALID, "idx and count are required");
+  if ((st = check_opt_ptr(idx, "idx")) != PI_OK || (st = check_opt_ptr(count, "count")) != PI_OK) return st;
+  const pi_ffn_desc& d = h->desc;
+  st = sparse_phases(h, x, batch, d.gated ? pik::GM_GATED : pik::GM_NONGATED, pik::ASRC_A, true, idx, count, 0,
+                     nullptr, nullptr, y, static_cast<hipStream_t>(stream));
+  return st == PI_OK ? ok() : st;
+}
+
+pi_status pi_ffn_profile_next(pi_ffn* h, int32_t phase, void* start_event, void* stop_event) {
+  if (h == nullptr) return fail(PI_ERR_INVALID, "handle is NULL");
+  if (phase < 0 || phase >= PI_PHASE_COUNT) return fail(PI_ERR_INVALID, "phase=%d is not a pi_phase", phase);
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PI_ERR_INVALID, "start_event and stop_event must both be set or both be NULL");
+  h->prof_start[phase] = start_event;
+  h->prof_stop[phase] = stop_event;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+/*
+ * pi_ffn.h -- C ABI of the activation-sparse ReLU FFN decode library (gfx950).
+ *
+ * One FFN layer of single-token (or small-batch) decode, computed only over the
+ * neurons that fire:
+ *
+ *   FFN(x) = ReLU(x W_gate^T + b) (.) (x W_up^T) W_down          (gated)
+ *   FFN(x) = ReLU(x W_up^T + b) W_down                          (non-gated)
+ *
+ * The FFN statement is the one in the PowerInfer paper explainer
+ * (0h-n0.github.io, "PowerInfer - コンシューマGPUでの高速LLM推論エンジン"),
+ * section "ニューロン活性化のべき乗則分布", FFN equation, with sigma = ReLU
+ * (the ReLU-sparse models named on the PowerInfer project page, section
+ * "サポートするモデル").  Which neurons are computed comes from one of three
+ * masks: the activation predictor (same explainer, section "活性化予測器":
+ * sigmoid(x W_p + b_p) > tau, here a rank-r two-layer ReLU MLP), the exact
+ * ReLU support, or every neuron.  Only selected neurons are computed (same
+ * explainer, section "GPU-CPUハイブリッドアーキテクチャ", inference flow; paper
+ * summary gptget.net "PowerInfer: Fast Large Language Model Serving with a
+ * Consumer-grade GPU", "Methodology": neuron-aware sparse operators).
+ *
+ * Conventions common to every call
+ * --------------------------------
+ * - Shapes: d = d_model, n = d_ffn, r = rank, B = tokens in the batch.
+ * - Every matrix is neuron-major and row-contiguous: W_gate, W_up [n][d];
+ *   the down projection is passed TRANSPOSED as W_downT [n][d], so row i holds
+ *   neuron i's down weights.  P1 [r][d], P2 [n][r].  x and y are [B][d].
+ * - dtypes: act (x, y) f32 or f16; weights f32, f16 or q4g32; predictor f32
+ *   or f16; b and b_p are always f32.  All accumulation is f32.
+ * - q4g32: each row is d/2 bytes, byte j holding element 2j in bits 0-3 and
+ *   element 2j+1 in bits 4-7 as 4-bit two's complement; scales are fp16
+ *   [n][d/32], one per 32 consecutive elements; value = q * s.
+ * - A batch shares one mask: the union of the per-token masks.
+ * - Index lists are int32, strictly ascending, unique; the count is one int32.
+ *   Both live in device memory and are never copied to the host.
+ * - Ownership: the caller allocates ALL device memory (weights, x, y, index
+ *   buffers, workspace).  The library never allocates device memory; its only
+ *   host allocation is the handle.  A handle borrows the weight and workspace
+ *   pointers until pi_ffn_destroy.
+ * - Streams: calls only enqueue work on `stream` (a hipStream_t passed as
+ *   void*, NULL = the null stream) and return without synchronising.  A
+ *   handle is not safe for concurrent use from two streams: it shares its
+ *   workspace between calls.  Handles whose calls are serialised on one
+ *   stream may share one workspace (e.g. the layers of a model).
+ * - Errors: every call returns a pi_status.  Arguments are validated on the
+ *   host before anything is enqueued; PI_ERR_INVALID means nothing was
+ *   enqueued.  PI_ERR_HIP reports a launch failure (or an earlier
+ *   asynchronous fault surfacing at launch).  pi_last_error() returns a
+ *   thread-local message for the last failing call on this thread.
+ * - Pointers: every device pointer must be 16-byte aligned.
+ */
+#ifndef PI_FFN_H
+#define PI_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PI_FFN_ABI_VERSION 1
+
+typedef enum pi_status {
+  PI_OK = 0,
+  PI_ERR_INVALID = 1,     /* bad argument; nothing enqueued */
+  PI_ERR_WORKSPACE = 2,   /* workspace missing or smaller than pi_ffn_workspace_bytes */
+  PI_ERR_HIP = 3,         /* HIP runtime error at launch */
+  PI_ERR_UNSUPPORTED = 4  /* valid request this build does not implement */
+} pi_status;
+
+typedef enum pi_dtype { PI_F32 = 0, PI_F16 = 1, PI_Q4G32 = 2 } pi_dtype;
+
+typedef enum pi_mask_mode {
+  PI_MASK_PREDICTED = 0,  /* predictor mask, then the sparse operator            */
+  PI_MASK_EXACT_RELU = 1, /* mask = {i : pre-activation > 0} from a dense pass    */
+  PI_MASK_DENSE = 2       /* every neuron, no predictor                          */
+} pi_mask_mode;
+
+/* Kernels a profiling event pair can bracket (pi_ffn_profile_next). */
+typedef enum pi_phase {
+  PI_PHASE_PRED_HIDDEN = 0, /* h = ReLU(x P1^T)                                  */
+  PI_PHASE_PRED_MASK = 1,   /* z = h P2^T + b_p, threshold, ballot, compaction    */
+  PI_PHASE_DENSE_PRE = 2,   /* exact mode: dense pre-activation, mask, compaction */
+  PI_PHASE_GATHER = 3,      /* row-gather GEMV: a = ReLU(gate) (.) up            */
+  PI_PHASE_DOWN = 4,        /* active-row down projection + fixed-order reduce    */
+  PI_PHASE_COUNT = 5
+} pi_phase;
+
+typedef struct pi_ffn_desc {
+  int32_t d_model;   /* d: > 0, multiple of 64                                  */
+  int32_t d_ffn;     /* n: > 0                                                  */
+  int32_t rank;      /* r: predictor rank, 0 = no predictor, else multiple of 64 */
+  int32_t gated;     /* 1 = gated (W_gate present), 0 = non-gated               */
+  int32_t max_batch; /* 1..16: largest B any call will pass                     */
+  int32_t w_dtype;   /* pi_dtype of W_gate, W_up, W_downT                       */
+  int32_t p_dtype;   /* PI_F32 or PI_F16: dtype of P1 and P2                     */
+  int32_t act_dtype; /* PI_F32 or PI_F16: dtype of x and y                       */
+  float tau;         /* predictor threshold on sigmoid(z), 0 < tau < 1          */
+} pi_ffn_desc;
+
+typedef struct pi_ffn_weights {
+  const void* w_gate;   /* [n][d] (q4g32: [n][d/2] bytes); NULL iff non-gated   */
+  const void* w_up;     /* [n][d]                                               */
+  const void* w_down_t; /* [n][d], row i = neuron i's down weights              */
+  const void* s_gate;   /* fp16 [n][d/32] iff q4g32 and gated, else NULL        */
+  const void* s_up;     /* fp16 [n][d/32] iff q4g32, else NULL                  */
+  const void* s_down;   /* fp16 [n][d/32] iff q4g32, else NULL                  */
+  const float* b;       /* [n] bias on the gate (gated) or on up (non-gated)    */
+  const void* p1;       /* [r][d] predictor first layer; NULL iff rank == 0     */
+  const void* p2;       /* [n][r] predictor second layer; NULL iff rank == 0    */
+  const float* b_p;     /* [n] predictor output bias; NULL iff rank == 0        */
+} pi_ffn_weights;
+
+typedef struct pi_ffn pi_ffn;
+
+/* ABI version this library was built with (PI_FFN_ABI_VERSION). */
+int32_t pi_ffn_abi_version(void);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* pi_last_error(void);
+
+/* Bytes of device workspace a handle with this descriptor needs.  Host only. */
+pi_status pi_ffn_workspace_bytes(const pi_ffn_desc* desc, size_t* bytes);
+
+/*
+ * Validate the descriptor and weights, bind them and the workspace to a new
+ * handle, and clear the workspace's counters with a kernel on `stream`,
+ * waiting for it before returning.  `workspace` is device memory of at least
+ * pi_ffn_workspace_bytes(desc) bytes, 256-byte aligned.
+ */
+pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        pi_ffn** out);
+
+/* Release the handle (host memory only; borrowed device memory is untouched). */
+pi_status pi_ffn_destroy(pi_ffn* h);
+
+/*
+ * Predictor and compaction alone.  For x [B][d]:
+ *   h = ReLU(x P1^T), z = h P2^T + b_p, selected_i = OR_t (z[t][i] > log(tau/(1-tau))),
+ * and writes idx[0..count) = ascending selected neurons (capacity n), *count.
+ * logits_dbg, if not NULL, receives z as f32 [B][n].  Requires rank > 0.
+ */
+pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx,
+                         int32_t* count, float* logits_dbg, void* stream);
+
+/*
+ * The whole step: mask (per mask_mode), compaction, the gathered activation
+ * a = ReLU(g) (.) u over the selected neurons only, and
+ * y[t] = sum over selected i of a[t][i] * W_downT[i], rounded once to act dtype.
+ * idx_out (capacity n) and count_out, if not NULL, receive the index list.
+ * With no neuron selected, y is +0.0.
+ */
+pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode,
+                         void* y, int32_t* idx_out, int32_t* count_out, void* stream);
+
+/*
+ * The sparse operator on a caller-given list: idx[0..*count) must be strictly
+ * ascending neuron ids in [0, n) (the list is read on the device; it is not
+ * validated), 0 <= *count <= n.  Computes the same y as pi_ffn_forward for
+ * that list.  count == 0 writes +0.0.
+ */
+pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx,
+                                const int32_t* count, void* y, void* stream);
+
+/*
+ * Profiling: arm a one-shot event pair.  The next launch of `phase`'s kernel
+ * by this handle is bracketed by hipEventRecord(start_event) and
+ * hipEventRecord(stop_event) on the launch stream; then the pair disarms.
+ * Events are hipEvent_t passed as void*.  Passing NULL events disarms.
+ */
+pi_status pi_ffn_profile_next(pi_ffn* h, int32_t phase, void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PI_FFN_H */

@@ -199,12 +199,31 @@ def forward(layer, x, mode: str = "predicted", weights=None) -> dict:
 
 
 def forward_masked(layer, x, idx, weights=None) -> dict:
-    """The sparse operator on a caller-given ascending index list."""
+    """The sparse operator on a caller-given ascending index list.
+
+    Only the listed neurons' rows are decoded and used: y_t = sum over i in idx
+    of ReLU(g_t[i]) u_t[i] W_downT[i].  Returns a (for the listed neurons, in
+    list order), y64 and y.
+    """
     xx = _f64(x)
-    w_gate, w_up, w_down_t = weights if weights is not None else _layer_weights(layer)
-    g, u = pre_activations(xx, w_gate, w_up, layer.b, layer.gated)
+    idx = np.asarray(idx, dtype=np.int64)
+
+    def rows(w, s):
+        if w is None:
+            return None
+        return dense_weights(np.asarray(w)[idx], None if s is None else np.asarray(s)[idx])
+
+    if weights is not None:
+        w_gate, w_up, w_down_t = (None if w is None else np.asarray(w)[idx] for w in weights)
+    else:
+        w_gate = rows(layer.w_gate, layer.s_gate) if layer.gated else None
+        w_up = rows(layer.w_up, layer.s_up)
+        w_down_t = rows(layer.w_down_t, layer.s_down)
+    g, u = pre_activations(xx, w_gate, w_up, np.asarray(layer.b)[idx], layer.gated)
     a = activations(g, u)
-    y64 = down_projection(a, w_down_t, idx)
+    y64 = down_projection(a, w_down_t, np.arange(idx.size))
+    if idx.size == 0:
+        y64 = np.zeros((xx.shape[0], xx.shape[1]), dtype=np.float64)
     return {"g": g, "u": u, "a": a, "y64": y64, "y": round_to_act(y64, layer.act_dtype)}
 
 

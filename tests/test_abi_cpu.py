@@ -1,0 +1,122 @@
+"""The C ABI library loads, exports every declared symbol, and validates on the host (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pi_ffn.h")
+
+
+def _pi():
+    import activation_sparse_decode_relu_amd as pi
+    return pi
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|pi_status|int32_t)\s+(pi_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    assert {"pi_ffn_create", "pi_ffn_predict", "pi_ffn_forward", "pi_ffn_forward_masked",
+            "pi_ffn_destroy", "pi_ffn_workspace_bytes", "pi_last_error"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol():
+    pi = _pi()
+    for name in declared_functions():
+        assert hasattr(pi.LIB, name), f"{name} is declared in pi_ffn.h but not exported"
+    assert set(declared_functions()) == set(pi.EXPORTED)
+    assert pi.LIB.pi_ffn_abi_version() == 1
+
+
+def test_struct_layouts_match_header():
+    pi = _pi()
+    assert ctypes.sizeof(pi.PiDesc) == 9 * 4
+    assert ctypes.sizeof(pi.PiWeights) == 10 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def _desc(**kw):
+    pi = _pi()
+    base = dict(d_model=4096, d_ffn=11008, rank=1024, gated=1, max_batch=1, w_dtype="f16", p_dtype="f16",
+                act_dtype="f16", tau=0.5)
+    base.update(kw)
+    return pi.make_desc(**base)
+
+
+@pytest.mark.parametrize("bad", [dict(d_model=100), dict(d_model=0), dict(d_ffn=0), dict(rank=65),
+                                 dict(rank=-64), dict(max_batch=0), dict(max_batch=17), dict(w_dtype=7),
+                                 dict(p_dtype=2), dict(act_dtype=2), dict(tau=0.0), dict(tau=1.0),
+                                 dict(gated=1, w_dtype="q4g32", d_model=96)])
+def test_invalid_descriptors(bad):
+    pi = _pi()
+    with pytest.raises(pi.PiError) as e:
+        pi.workspace_bytes(_desc(**bad))
+    assert e.value.status == 1
+    assert pi.last_error()
+
+
+def test_workspace_grows_with_batch_and_rank():
+    pi = _pi()
+    b1 = pi.workspace_bytes(_desc(max_batch=1))
+    b16 = pi.workspace_bytes(_desc(max_batch=16))
+    r0 = pi.workspace_bytes(_desc(rank=0))
+    assert b16 > b1 > r0 > 0
+    assert b1 % 256 == 0
+
+
+def _create(desc, weights, ws_ptr=None, ws_bytes=0):
+    pi = _pi()
+    handle = ctypes.c_void_p()
+    st = pi.LIB.pi_ffn_create(ctypes.byref(desc), ctypes.byref(weights), ws_ptr, ws_bytes, None,
+                              ctypes.byref(handle))
+    return st, handle
+
+
+def _weights(**kw):
+    pi = _pi()
+    fake = 0x10000
+    base = dict(w_gate=fake, w_up=fake, w_down_t=fake, s_gate=None, s_up=None, s_down=None, b=fake,
+                p1=fake, p2=fake, b_p=fake)
+    base.update(kw)
+    return pi.PiWeights(*[base[k] for k, _ in pi.PiWeights._fields_])
+
+
+@pytest.mark.parametrize("bad", [dict(w_gate=None), dict(w_up=None), dict(b=None), dict(p1=None),
+                                 dict(s_up=0x10000), dict(w_down_t=0x10004)])
+def test_create_rejects_bad_weights_before_any_gpu_call(bad):
+    st, handle = _create(_desc(), _weights(**bad))
+    assert st == 1 and not handle.value
+
+
+def test_create_rejects_small_or_misaligned_workspace():
+    pi = _pi()
+    need = pi.workspace_bytes(_desc())
+    st, _ = _create(_desc(), _weights(), None, need)
+    assert st == 2
+    st, _ = _create(_desc(), _weights(), 0x10000, need - 1)
+    assert st == 2
+    st, _ = _create(_desc(), _weights(), 0x10080, need)
+    assert st == 2
+
+
+def test_null_handle_calls_are_invalid():
+    pi = _pi()
+    assert pi.LIB.pi_ffn_forward(None, 0x1000, 1, 0, 0x1000, None, None, None) == 1
+    assert pi.LIB.pi_ffn_predict(None, 0x1000, 1, 0x1000, 0x1000, None, None) == 1
+    assert pi.LIB.pi_ffn_forward_masked(None, 0x1000, 1, 0x1000, 0x1000, 0x1000, None) == 1
+    assert pi.LIB.pi_ffn_destroy(None) == 1
+    assert pi.LIB.pi_ffn_profile_next(None, 0, None, None) == 1
+
+
+def test_package_fails_loudly_without_library(tmp_path):
+    import subprocess
+    import sys
+    env = dict(os.environ, PI_FFN_LIB=str(tmp_path / "missing.so"))
+    res = subprocess.run([sys.executable, "-c", "import activation_sparse_decode_relu_amd"], cwd=ROOT, env=env,
+                         capture_output=True, text=True)
+    assert res.returncode != 0 and "ImportError" in res.stderr
