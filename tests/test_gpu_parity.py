@@ -87,7 +87,8 @@ def test_toy_config_tokens(mode):
             assert np.array_equal(idx, np.arange(layer.d_ffn))
         ref = oracle.forward_masked(layer, xt, idx)["y64"]
         assert rel_l2_rows(y, ref).max() <= tol_for(layer.act_dtype)
-    assert ambiguous <= 2
+    # the band is a worst-case bound: decisions inside it are accepted either way; keep them rare
+    assert ambiguous <= 0.01 * x.shape[0] * layer.d_ffn, ambiguous
     h.close()
 
 
