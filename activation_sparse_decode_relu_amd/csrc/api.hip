@@ -3,11 +3,11 @@
 //
 // Sequences (PowerInfer paper explainer, section "GPU-CPUハイブリッドアーキテクチャ",
 // inference flow: predict, then compute only the predicted neurons):
-//   predict            pred_hidden -> rows_mask(P2, h)             -> idx, count
-//   forward PREDICTED  pred_hidden -> rows_mask(P2, h) -> gather -> down
-//   forward EXACT      rows_mask(W_gate|W_up, x) -> [gather(up only)] -> down
-//   forward DENSE      gather(all neurons) -> down(all neurons)
-//   forward_masked     gather(caller list) -> down(caller list)
+//   predict            pred_hidden -> ffn_group(mask only) -> finish(index list)
+//   forward PREDICTED  pred_hidden -> ffn_group(predictor mask) -> finish
+//   forward EXACT      ffn_group(dense pre-activation mask) -> finish
+//   forward DENSE      ffn_group(every neuron) -> finish
+//   forward_masked     ffn_group(caller's list) -> finish
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -41,9 +41,6 @@ pi_status ok() {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxBatch = 16;
-constexpr int kMaxSplits = 64;       // neuron slices of the down projection
-constexpr int kDownTargetWG = 256;   // workgroups the down projection aims for
-constexpr int kGatherMaxWG = 1024;   // persistent gather grid cap (4 waves each)
 constexpr int kMaxD = 1 << 20;
 constexpr int kMaxN = 1 << 24;
 
@@ -51,27 +48,37 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t tickets, h, mask, idx, count, g, a, partial, total;
-  int n_tickets, n_tiles, splits;
+  size_t h, mask, idx, count, partial, total;
+  int group, waves, n_groups, n_words;
 };
+
+// Neurons per group workgroup and waves per workgroup for a layer.  Small
+// layers use 32-neuron groups of 4 waves so that every compute unit gets work;
+// large layers use 128-neuron groups of 8 waves, which keeps the group
+// partials (groups x d floats) small.
+void group_shape(int n, int* group, int* waves) {
+  const int g32 = (n + 31) / 32;
+  if (g32 <= 512) {
+    *group = 32;
+    *waves = 4;
+  } else {
+    *group = 128;
+    *waves = 8;
+  }
+}
 
 Layout layout_for(const pi_ffn_desc& d) {
   Layout L{};
   const size_t B = (size_t)d.max_batch, n = (size_t)d.d_ffn, dm = (size_t)d.d_model;
-  const int tw = pik::down_tile_width(d.w_dtype);
-  L.n_tiles = (d.d_model + tw - 1) / tw;
-  int s = kDownTargetWG / L.n_tiles;
-  L.splits = s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
-  L.n_tickets = 2 + L.n_tiles;  // [0] predictor mask, [1] dense pre-activation, [2..] down tiles
+  group_shape(d.d_ffn, &L.group, &L.waves);
+  L.n_groups = (d.d_ffn + L.group - 1) / L.group;
+  L.n_words = (d.d_ffn + 31) / 32;
   size_t off = 0;
-  L.tickets = off; off = align_up(off + sizeof(unsigned) * L.n_tickets);
   L.h = off;       off = align_up(off + sizeof(float) * B * (size_t)(d.rank > 0 ? d.rank : 1));
-  L.mask = off;    off = align_up(off + sizeof(unsigned long long) * ((n + 63) / 64));
+  L.mask = off;    off = align_up(off + sizeof(unsigned) * (size_t)L.n_words);
   L.idx = off;     off = align_up(off + sizeof(int) * n);
   L.count = off;   off = align_up(off + sizeof(int));
-  L.g = off;       off = align_up(off + sizeof(float) * B * n);
-  L.a = off;       off = align_up(off + sizeof(float) * B * n);
-  L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.splits * B * dm);
+  L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.n_groups * B * dm);
   L.total = off;
   return L;
 }
@@ -95,6 +102,10 @@ pi_status check_desc(const pi_ffn_desc* d) {
     return fail(PI_ERR_INVALID, "act_dtype=%d must be PI_F32 or PI_F16", d->act_dtype);
   if (d->rank > 0 && !(d->tau > 0.0f && d->tau < 1.0f))
     return fail(PI_ERR_INVALID, "tau=%g must lie in (0, 1)", (double)d->tau);
+  int group, waves;
+  group_shape(d->d_ffn, &group, &waves);
+  if (pik::group_cpl(d->w_dtype, d->d_model, waves) == 0)
+    return fail(PI_ERR_UNSUPPORTED, "d_model=%d is larger than this build's per-wave slice allows", d->d_model);
   return PI_OK;
 }
 
@@ -125,17 +136,13 @@ struct pi_ffn {
   size_t ws_bytes;
   Layout L;
   float thr;
-  int gather_grid;
   void* prof_start[PI_PHASE_COUNT];
   void* prof_stop[PI_PHASE_COUNT];
 
-  unsigned* tickets() const { return reinterpret_cast<unsigned*>(ws + L.tickets); }
   float* h() const { return reinterpret_cast<float*>(ws + L.h); }
-  unsigned long long* mask() const { return reinterpret_cast<unsigned long long*>(ws + L.mask); }
+  unsigned* mask() const { return reinterpret_cast<unsigned*>(ws + L.mask); }
   int* idx() const { return reinterpret_cast<int*>(ws + L.idx); }
   int* count() const { return reinterpret_cast<int*>(ws + L.count); }
-  float* g() const { return reinterpret_cast<float*>(ws + L.g); }
-  float* a() const { return reinterpret_cast<float*>(ws + L.a); }
   float* partial() const { return reinterpret_cast<float*>(ws + L.partial); }
 };
 
@@ -172,33 +179,60 @@ pi_status check_opt_ptr(const void* p, const char* name) {
   return PI_OK;
 }
 
-// Predictor mask: h = ReLU(x P1^T), then logits, threshold, ballot, compaction.
-pi_status predictor_phases(pi_ffn* h, const void* x, int B, int* idx, int* count, float* logits, hipStream_t s) {
+// Index lists and counts are read and written as single int32 values.
+pi_status check_int_ptr(const void* p, const char* name) {
+  if (p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) != 0)
+    return fail(PI_ERR_INVALID, "%s is not 4-byte aligned", name);
+  return PI_OK;
+}
+
+pik::GroupArgs group_args(const pi_ffn* h, const void* x, int B) {
   const pi_ffn_desc& d = h->desc;
-  pi_status st = run_phase(h, PI_PHASE_PRED_HIDDEN, s, "pred_hidden", [&] {
+  pik::GroupArgs a{};
+  a.w_gate = h->w.w_gate;
+  a.w_up = h->w.w_up;
+  a.w_down_t = h->w.w_down_t;
+  a.s_gate = static_cast<const _Float16*>(h->w.s_gate);
+  a.s_up = static_cast<const _Float16*>(h->w.s_up);
+  a.s_down = static_cast<const _Float16*>(h->w.s_down);
+  a.b = h->w.b;
+  a.p2 = h->w.p2;
+  a.b_p = h->w.b_p;
+  a.h = h->h();
+  a.x = x;
+  a.mask_words = h->mask();
+  a.partial = h->partial();
+  a.thr = h->thr;
+  a.p_dtype = d.p_dtype;
+  a.d = d.d_model;
+  a.n = d.d_ffn;
+  a.r = d.rank;
+  a.B = B;
+  a.G = h->L.group;
+  a.nw = h->L.waves;
+  a.gated = d.gated;
+  return a;
+}
+
+pi_status hidden_phase(pi_ffn* h, const void* x, int B, hipStream_t s) {
+  const pi_ffn_desc& d = h->desc;
+  return run_phase(h, PI_PHASE_PRED_HIDDEN, s, "pred_hidden", [&] {
     return pik::launch_pred_hidden(d.p_dtype, d.act_dtype, h->w.p1, x, d.d_model, d.rank, B, h->h(), s);
-  });
-  if (st != PI_OK) return st;
-  return run_phase(h, PI_PHASE_PRED_MASK, s, "pred_mask", [&] {
-    return pik::launch_rows_mask(d.p_dtype, PI_F32, h->w.p2, nullptr, h->h(), d.rank, d.d_ffn, h->w.b_p, h->thr, B,
-                                 logits, h->mask(), h->tickets() + 0, idx, count, s);
   });
 }
 
-pi_status sparse_phases(pi_ffn* h, const void* x, int B, int gm, int asrc, bool gather, const int* idx,
-                        const int* count, int dense, int* iota_out, int* count_out, void* y, hipStream_t s) {
+pi_status group_phase(pi_ffn* h, int mode, const pik::GroupArgs& a, hipStream_t s) {
+  return run_phase(h, PI_PHASE_GROUP, s, "ffn_group",
+                   [&] { return pik::launch_ffn_group(h->desc.w_dtype, h->desc.act_dtype, mode, a, s); });
+}
+
+// reduce: sum the group partials into y; list: 0 = none, 1 = compact the mask words, 2 = 0..n-1
+pi_status finish_phase(pi_ffn* h, int B, void* y, bool reduce, int list, int* idx, int* count, hipStream_t s) {
   const pi_ffn_desc& d = h->desc;
-  if (gather) {
-    pi_status st = run_phase(h, PI_PHASE_GATHER, s, "gather", [&] {
-      return pik::launch_gather(d.w_dtype, d.act_dtype, gm, h->w.w_gate, h->w.w_up, h->w.s_gate, h->w.s_up, h->w.b,
-                                h->g(), x, d.d_model, d.d_ffn, B, idx, count, dense, h->a(), iota_out, count_out,
-                                h->gather_grid, s);
-    });
-    if (st != PI_OK) return st;
-  }
-  return run_phase(h, PI_PHASE_DOWN, s, "down", [&] {
-    return pik::launch_down(d.w_dtype, d.act_dtype, asrc, h->w.w_down_t, h->w.s_down, h->a(), h->g(), d.d_model,
-                            d.d_ffn, B, idx, count, dense, h->L.splits, h->partial(), h->tickets() + 2, y, s);
+  return run_phase(h, PI_PHASE_FINISH, s, "finish", [&] {
+    return pik::launch_finish(d.act_dtype, h->partial(), h->L.n_groups, B, d.d_model, y,
+                              list == 1 ? h->mask() : nullptr, h->L.n_words, list == 2 ? d.d_ffn : 0, idx, count,
+                              reduce, list != 0, s);
   });
 }
 
@@ -240,11 +274,10 @@ pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights, 
   h->ws_bytes = workspace_bytes;
   h->L = L;
   h->thr = desc->rank > 0 ? (float)std::log((double)desc->tau / (1.0 - (double)desc->tau)) : 0.0f;
-  const int want = (desc->d_ffn + 3) / 4;
-  h->gather_grid = want < kGatherMaxWG ? want : kGatherMaxWG;
 
+  // Clear the mask words once so a predict() before any forward() never reads garbage.
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pik::launch_fill_u32(h->tickets(), L.n_tickets, 0u, s);
+  hipError_t e = pik::launch_fill_u32(h->mask(), L.n_words, 0u, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete h;
@@ -266,54 +299,53 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, 
   if (st != PI_OK) return st;
   if (h->desc.rank == 0) return fail(PI_ERR_INVALID, "predict needs a predictor (rank > 0)");
   if (idx == nullptr || count == nullptr) return fail(PI_ERR_INVALID, "idx and count are required");
-  if ((st = check_opt_ptr(idx, "idx")) != PI_OK || (st = check_opt_ptr(count, "count")) != PI_OK ||
+  if ((st = check_int_ptr(idx, "idx")) != PI_OK || (st = check_int_ptr(count, "count")) != PI_OK ||
       (st = check_opt_ptr(logits_dbg, "logits_dbg")) != PI_OK)
     return st;
-  st = predictor_phases(h, x, batch, idx, count, logits_dbg, static_cast<hipStream_t>(stream));
-  return st == PI_OK ? ok() : st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pik::GroupArgs a = group_args(h, x, batch);
+  a.logits = logits_dbg;
+  a.mask_only = 1;
+  if ((st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
+  if ((st = group_phase(h, pik::MODE_PRED, a, s)) != PI_OK) return st;
+  if ((st = finish_phase(h, batch, nullptr, false, 1, idx, count, s)) != PI_OK) return st;
+  return ok();
 }
 
 pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
                          int32_t* count_out, void* stream) {
   pi_status st = check_call(h, x, batch, y, true);
   if (st != PI_OK) return st;
-  if ((st = check_opt_ptr(idx_out, "idx_out")) != PI_OK || (st = check_opt_ptr(count_out, "count_out")) != PI_OK)
+  if ((st = check_int_ptr(idx_out, "idx_out")) != PI_OK || (st = check_int_ptr(count_out, "count_out")) != PI_OK)
     return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const pi_ffn_desc& d = h->desc;
+  const bool want_list = idx_out != nullptr || count_out != nullptr;
   int* idx = idx_out != nullptr ? idx_out : h->idx();
   int* count = count_out != nullptr ? count_out : h->count();
+  pik::GroupArgs a = group_args(h, x, batch);
+  int mode, list;
   switch (mask_mode) {
     case PI_MASK_PREDICTED:
       if (d.rank == 0) return fail(PI_ERR_INVALID, "PREDICTED mode needs a predictor (rank > 0)");
-      st = predictor_phases(h, x, batch, idx, count, nullptr, s);
-      if (st == PI_OK)
-        st = sparse_phases(h, x, batch, d.gated ? pik::GM_GATED : pik::GM_NONGATED, pik::ASRC_A, true, idx, count,
-                           0, nullptr, nullptr, y, s);
+      mode = pik::MODE_PRED;
+      list = 1;
       break;
     case PI_MASK_EXACT_RELU:
-      st = run_phase(h, PI_PHASE_DENSE_PRE, s, "dense_pre", [&] {
-        return pik::launch_rows_mask(d.w_dtype, d.act_dtype, d.gated ? h->w.w_gate : h->w.w_up,
-                                     d.gated ? h->w.s_gate : h->w.s_up, x, d.d_model, d.d_ffn, h->w.b, 0.0f, batch,
-                                     h->g(), h->mask(), h->tickets() + 1, idx, count, s);
-      });
-      if (st == PI_OK) {
-        if (d.gated)
-          st = sparse_phases(h, x, batch, pik::GM_EXACT_GATED, pik::ASRC_A, true, idx, count, 0, nullptr, nullptr, y,
-                             s);
-        else
-          st = sparse_phases(h, x, batch, pik::GM_NONGATED, pik::ASRC_GRELU, false, idx, count, 0, nullptr, nullptr,
-                             y, s);
-      }
+      mode = pik::MODE_EXACT;
+      list = 1;
       break;
     case PI_MASK_DENSE:
-      st = sparse_phases(h, x, batch, d.gated ? pik::GM_GATED : pik::GM_NONGATED, pik::ASRC_A, true, nullptr,
-                         nullptr, 1, idx_out, count_out, y, s);
+      mode = pik::MODE_DENSE;
+      list = 2;
       break;
     default:
       return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
   }
-  return st == PI_OK ? ok() : st;
+  if (mode == pik::MODE_PRED && (st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
+  if ((st = group_phase(h, mode, a, s)) != PI_OK) return st;
+  if ((st = finish_phase(h, batch, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
+  return ok();
 }
 
 pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx, const int32_t* count,
@@ -321,11 +353,14 @@ pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const i
   pi_status st = check_call(h, x, batch, y, true);
   if (st != PI_OK) return st;
   if (idx == nullptr || count == nullptr) return fail(PI_ERR_INVALID, "idx and count are required");
-  if ((st = check_opt_ptr(idx, "idx")) != PI_OK || (st = check_opt_ptr(count, "count")) != PI_OK) return st;
-  const pi_ffn_desc& d = h->desc;
-  st = sparse_phases(h, x, batch, d.gated ? pik::GM_GATED : pik::GM_NONGATED, pik::ASRC_A, true, idx, count, 0,
-                     nullptr, nullptr, y, static_cast<hipStream_t>(stream));
-  return st == PI_OK ? ok() : st;
+  if ((st = check_int_ptr(idx, "idx")) != PI_OK || (st = check_int_ptr(count, "count")) != PI_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pik::GroupArgs a = group_args(h, x, batch);
+  a.list = idx;
+  a.list_count = count;
+  if ((st = group_phase(h, pik::MODE_LIST, a, s)) != PI_OK) return st;
+  if ((st = finish_phase(h, batch, y, true, 0, nullptr, nullptr, s)) != PI_OK) return st;
+  return ok();
 }
 
 pi_status pi_ffn_profile_next(pi_ffn* h, int32_t phase, void* start_event, void* stop_event) {

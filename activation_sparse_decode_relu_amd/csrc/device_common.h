@@ -53,90 +53,133 @@ __device__ __forceinline__ f16x2 q4pair(unsigned t) {
   return as_h2(hb) - bias;
 }
 
-// acc += sum over the chunk's elements of w_e * v_e   (v points at the chunk's first element)
+// The EPC vector elements matching one 16-byte weight chunk, held in registers.
 template <int WT, int VT>
-__device__ __forceinline__ void dot_chunk(float& acc, u32x4 w, const typename VecT<VT>::T* v, float scale);
+struct XChunk {
+  static constexpr int WORDS = WFmt<WT>::EPC * (int)sizeof(typename VecT<VT>::T) / 4;
+  unsigned w[WORDS];
+  __device__ __forceinline__ void load(const typename VecT<VT>::T* p) {
+    if constexpr (WORDS == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int k = 0; k < WORDS / 4; ++k) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(p)[k];
+        w[4 * k] = v.x;
+        w[4 * k + 1] = v.y;
+        w[4 * k + 2] = v.z;
+        w[4 * k + 3] = v.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int k = 0; k < WORDS; ++k) w[k] = 0u;
+  }
+  __device__ __forceinline__ float f(int k) const { return __builtin_bit_cast(float, w[k]); }
+};
+
+// acc += sum over the chunk's elements of w_e * x_e   (q4: the group scale applied once)
+template <int WT, int VT>
+__device__ __forceinline__ void dot_chunk(float& acc, u32x4 w, const XChunk<WT, VT>& x, float scale);
 
 template <>
-__device__ __forceinline__ void dot_chunk<DT_F16, DT_F16>(float& acc, u32x4 w, const f16* v, float) {
-  const u32x4 xv = *reinterpret_cast<const u32x4*>(v);
-  acc = fdot2u(w.x, xv.x, acc);
-  acc = fdot2u(w.y, xv.y, acc);
-  acc = fdot2u(w.z, xv.z, acc);
-  acc = fdot2u(w.w, xv.w, acc);
+__device__ __forceinline__ void dot_chunk<DT_F16, DT_F16>(float& acc, u32x4 w, const XChunk<DT_F16, DT_F16>& x,
+                                                          float) {
+  acc = fdot2u(w.x, x.w[0], acc);
+  acc = fdot2u(w.y, x.w[1], acc);
+  acc = fdot2u(w.z, x.w[2], acc);
+  acc = fdot2u(w.w, x.w[3], acc);
 }
 
 template <>
-__device__ __forceinline__ void dot_chunk<DT_F32, DT_F32>(float& acc, u32x4 w, const float* v, float) {
-  const f32x4 xv = *reinterpret_cast<const f32x4*>(v);
+__device__ __forceinline__ void dot_chunk<DT_F32, DT_F32>(float& acc, u32x4 w, const XChunk<DT_F32, DT_F32>& x,
+                                                          float) {
   const f32x4 wv = __builtin_bit_cast(f32x4, w);
-  acc = fmaf(wv.x, xv.x, acc);
-  acc = fmaf(wv.y, xv.y, acc);
-  acc = fmaf(wv.z, xv.z, acc);
-  acc = fmaf(wv.w, xv.w, acc);
+  acc = fmaf(wv.x, x.f(0), acc);
+  acc = fmaf(wv.y, x.f(1), acc);
+  acc = fmaf(wv.z, x.f(2), acc);
+  acc = fmaf(wv.w, x.f(3), acc);
 }
 
 template <>
-__device__ __forceinline__ void dot_chunk<DT_F16, DT_F32>(float& acc, u32x4 w, const float* v, float) {
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(v);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(v + 4);
-  f16x2 h;
-  h = as_h2(w.x); acc = fmaf((float)h.x, x0.x, acc); acc = fmaf((float)h.y, x0.y, acc);
-  h = as_h2(w.y); acc = fmaf((float)h.x, x0.z, acc); acc = fmaf((float)h.y, x0.w, acc);
-  h = as_h2(w.z); acc = fmaf((float)h.x, x1.x, acc); acc = fmaf((float)h.y, x1.y, acc);
-  h = as_h2(w.w); acc = fmaf((float)h.x, x1.z, acc); acc = fmaf((float)h.y, x1.w, acc);
+__device__ __forceinline__ void dot_chunk<DT_F16, DT_F32>(float& acc, u32x4 w, const XChunk<DT_F16, DT_F32>& x,
+                                                          float) {
+  const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const f16x2 h = as_h2(ws[p]);
+    acc = fmaf((float)h.x, x.f(2 * p), acc);
+    acc = fmaf((float)h.y, x.f(2 * p + 1), acc);
+  }
 }
 
 template <>
-__device__ __forceinline__ void dot_chunk<DT_F32, DT_F16>(float& acc, u32x4 w, const f16* v, float) {
-  const u32x2 xv = *reinterpret_cast<const u32x2*>(v);
+__device__ __forceinline__ void dot_chunk<DT_F32, DT_F16>(float& acc, u32x4 w, const XChunk<DT_F32, DT_F16>& x,
+                                                          float) {
   const f32x4 wv = __builtin_bit_cast(f32x4, w);
-  f16x2 h;
-  h = as_h2(xv.x); acc = fmaf(wv.x, (float)h.x, acc); acc = fmaf(wv.y, (float)h.y, acc);
-  h = as_h2(xv.y); acc = fmaf(wv.z, (float)h.x, acc); acc = fmaf(wv.w, (float)h.y, acc);
+  f16x2 h = as_h2(x.w[0]);
+  acc = fmaf(wv.x, (float)h.x, acc);
+  acc = fmaf(wv.y, (float)h.y, acc);
+  h = as_h2(x.w[1]);
+  acc = fmaf(wv.z, (float)h.x, acc);
+  acc = fmaf(wv.w, (float)h.y, acc);
 }
 
-// int4 group of 32: acc += s * sum_e q_e v_e.  q_e * v_e is exact in fp32 (fp16 x small int).
+// int4 group of 32: acc += s * sum_e q_e x_e.  q_e * x_e is exact in fp32 (fp16 x small int).
 template <>
-__device__ __forceinline__ void dot_chunk<DT_Q4, DT_F16>(float& acc, u32x4 w, const f16* v, float scale) {
-  const u32x4* xp = reinterpret_cast<const u32x4*>(v);
+__device__ __forceinline__ void dot_chunk<DT_Q4, DT_F16>(float& acc, u32x4 w, const XChunk<DT_Q4, DT_F16>& x,
+                                                         float scale) {
   float g = 0.f;
   const unsigned words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const u32x4 xv = xp[k];
     const unsigned q = words[k] ^ 0x88888888u;
-    g = fdot2(q4pair(q), as_h2(xv.x), g);
-    g = fdot2(q4pair(q >> 8), as_h2(xv.y), g);
-    g = fdot2(q4pair(q >> 16), as_h2(xv.z), g);
-    g = fdot2(q4pair(q >> 24), as_h2(xv.w), g);
+    g = fdot2(q4pair(q), as_h2(x.w[4 * k]), g);
+    g = fdot2(q4pair(q >> 8), as_h2(x.w[4 * k + 1]), g);
+    g = fdot2(q4pair(q >> 16), as_h2(x.w[4 * k + 2]), g);
+    g = fdot2(q4pair(q >> 24), as_h2(x.w[4 * k + 3]), g);
   }
   acc = fmaf(g, scale, acc);
 }
 
 template <>
-__device__ __forceinline__ void dot_chunk<DT_Q4, DT_F32>(float& acc, u32x4 w, const float* v, float scale) {
+__device__ __forceinline__ void dot_chunk<DT_Q4, DT_F32>(float& acc, u32x4 w, const XChunk<DT_Q4, DT_F32>& x,
+                                                         float scale) {
   float g = 0.f;
   const unsigned words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(v + 8 * k);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(v + 8 * k + 4);
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int q = (int)((words[k] >> (4 * e)) & 0xFu) - (int)(((words[k] >> (4 * e)) & 0x8u) << 1);
-      g = fmaf((float)q, xs[e], g);
+      const unsigned nib = (words[k] >> (4 * e)) & 0xFu;
+      const int q = (int)nib - (int)((nib & 0x8u) << 1);
+      g = fmaf((float)q, x.f(8 * k + e), g);
     }
   }
   acc = fmaf(g, scale, acc);
 }
 
-// Sum over the 64 lanes; every lane returns lane 0's result (one fixed association order).
+// Sum over the 64 lanes, returned uniformly to every lane.  Within each row
+// of 16 lanes, DPP swaps (adjacent lanes, adjacent pairs, half-row mirror, row
+// mirror) leave the row total, bitwise identical, in all 16 lanes; the four
+// row totals are then added in a fixed order.  No LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shuffled(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  v += dpp_shuffled<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_shuffled<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_shuffled<0x141>(v);  // row_half_mirror
+  v += dpp_shuffled<0x140>(v);  // row_mirror
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);

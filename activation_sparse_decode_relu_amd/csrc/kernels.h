@@ -6,29 +6,44 @@
 
 namespace pik {
 
-enum : int { GM_GATED = 0, GM_NONGATED = 1, GM_EXACT_GATED = 2 };
-enum : int { ASRC_A = 0, ASRC_GRELU = 1 };
+enum : int { MODE_PRED = 0, MODE_EXACT = 1, MODE_DENSE = 2, MODE_LIST = 3 };
 
-// Output columns owned by one down-projection workgroup.
-int down_tile_width(int wt);
+constexpr int kMaxTokens = 16;
+
+// Everything one k_ffn_group launch reads and writes (passed by value).
+struct GroupArgs {
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down_t;
+  const _Float16* s_gate;
+  const _Float16* s_up;
+  const _Float16* s_down;
+  const float* b;
+  const void* p2;          // predictor second layer [n][r] (MODE_PRED)
+  const float* b_p;        // predictor bias [n] (MODE_PRED)
+  const float* h;          // predictor hidden [B][r] (MODE_PRED)
+  const void* x;           // [B][d]
+  const int* list;         // MODE_LIST: caller's ascending neuron ids
+  const int* list_count;   // MODE_LIST: device int
+  float* logits;           // MODE_PRED, optional: z [B][n]
+  unsigned* mask_words;    // MODE_PRED / MODE_EXACT: [ceil(n/32)], bit b of word w = neuron 32w+b
+  float* partial;          // [groups][B][d]
+  float thr;
+  int p_dtype, d, n, r, B, G, nw, gated, mask_only;
+};
+
+// Chunks per lane of a wave's d-slice with nw waves per workgroup (1, 2 or 4), or 0 if d is too large.
+int group_cpl(int wt, int d, int nw);
 
 hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t s);
 
 hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int d, int r, int B, float* h,
                               hipStream_t s);
 
-hipError_t launch_rows_mask(int wt, int vt, const void* rows, const void* scales, const void* vec, int K, int n,
-                            const float* bias, float thr, int B, float* vals_out,
-                            unsigned long long* mask_words, unsigned* ticket, int* idx_out, int* count_out,
-                            hipStream_t s);
+hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s);
 
-hipError_t launch_gather(int wt, int at, int gm, const void* w_gate, const void* w_up, const void* s_gate,
-                         const void* s_up, const float* bias, const float* g_ws, const void* x, int d, int n,
-                         int B, const int* idx, const int* count, int dense, float* a_ws, int* iota_out,
-                         int* count_out, int grid, hipStream_t s);
-
-hipError_t launch_down(int wt, int ot, int asrc, const void* w_down_t, const void* s_down, const float* a_ws,
-                       const float* g_ws, int d, int n, int B, const int* idx, const int* count, int dense,
-                       int S, float* partial, unsigned* tickets, void* y, hipStream_t s);
+hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
+                         const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,
+                         bool reduce, bool index_list, hipStream_t s);
 
 }  // namespace pik

@@ -3,47 +3,34 @@
 // The step (PowerInfer paper explainer, section "活性化予測器" for the
 // predictor, section "ニューロン活性化のべき乗則分布" for the FFN equation,
 // section "GPU-CPUハイブリッドアーキテクチャ" for "compute only the predicted
-// neurons"):
+// neurons"), three kernels per call:
 //
-//   k_pred_hidden   h = ReLU(x P1^T)                               HBM-bound GEMV
-//   k_rows_mask     v = rows . vec + bias; selected = OR_t v > thr;
-//                   wave ballot -> 64-bit mask words; the last workgroup
-//                   compacts the words into the ascending index list  HBM-bound GEMV
-//   k_gather        for each selected neuron: a = ReLU(g) (.) u        row-gather GEMV
-//   k_down          y = sum over selected i of a_i W_downT[i]: split over
-//                   (column tile, neuron slice); fixed-order sum of the
-//                   slices by the last workgroup of each tile; no atomics
-//                   on values
+//   k_pred_hidden  h = ReLU(x P1^T)                                   HBM-bound GEMV
+//   k_ffn_group    one workgroup per group of G neurons:
+//                    mask   predictor logits z = h P2^T + b_p (or the dense
+//                           pre-activation in exact mode), threshold, wave
+//                           ballot -> the group's 64-bit mask words;
+//                    gather the selected neurons' gate/up/down rows: each of
+//                           the 8 waves owns one d-slice, so every row is read
+//                           by 8 waves in 1 KiB pieces and the down rows are
+//                           prefetched with the gate/up rows;
+//                    act    a = ReLU(g) (.) u from a fixed-order sum of the
+//                           waves' partial dot products;
+//                    down   the group's partial y over its own neurons, each
+//                           wave writing only its d-slice (no cross-wave sum).
+//   k_finish       y = sum of the group partials in a fixed order (no atomics),
+//                  plus one extra workgroup that compacts the mask words into
+//                  the ascending index list.
 //
-// Every loop that reads weights issues 16-byte loads from 64 consecutive
-// chunks of a row (1 KiB per wave instruction), several rows and chunks in
-// flight per lane.  Reductions use one fixed order, so results are
-// bit-reproducible run to run for a given launch shape.
+// No kernel communicates between workgroups inside a launch; every hand-off
+// goes through a kernel boundary.  Reductions use one fixed order, so results
+// are bit-reproducible run to run.
 #include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
 
 namespace pik {
-
-// ---------------------------------------------------------------------------
-// Cross-workgroup hand-off: the last workgroup to arrive at a ticket sees
-// every other workgroup's stores (release fence before the ticket, acquire
-// fence after it).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool arrive_last(unsigned* ticket, unsigned expected) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(ticket, 1u);
-    s_last = (prev == expected - 1u) ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
 
 // Exclusive prefix sum over the workgroup; *total gets the sum of all values.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
@@ -69,23 +56,24 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
   return before + incl - v;
 }
 
-// Mask words -> ascending int32 indices + count, by one workgroup.  Each
-// thread owns a contiguous run of words; a scan of the per-thread popcounts
-// gives every thread its output offset, so the list comes out in order.
-__device__ void block_compact(const unsigned long long* words, int n_words, int* idx, int* count) {
+// Mask words (bit b of word w = neuron 32w + b) -> ascending int32 indices +
+// count, by one workgroup.  Each thread owns a contiguous run of words; a scan
+// of the per-thread popcounts gives every thread its output offset, so the
+// list comes out in order.
+__device__ void block_compact(const unsigned* words, int n_words, int* idx, int* count) {
   const int T = blockDim.x, tid = threadIdx.x;
   const int wpt = (n_words + T - 1) / T;
   const int w0 = min(tid * wpt, n_words), w1 = min(w0 + wpt, n_words);
   int c = 0;
-  for (int w = w0; w < w1; ++w) c += __popcll(__hip_atomic_load(words + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  for (int w = w0; w < w1; ++w) c += __popc(words[w]);
   int total;
   int pos = block_exclusive_scan(c, &total);
   for (int w = w0; w < w1; ++w) {
-    unsigned long long m = __hip_atomic_load(words + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned m = words[w];
     while (m) {
-      const int b = __ffsll((long long)m) - 1;
-      idx[pos++] = w * 64 + b;
-      m &= m - 1ull;
+      const int b = __ffs((int)m) - 1;
+      idx[pos++] = w * 32 + b;
+      m &= m - 1u;
     }
   }
   if (tid == 0) *count = total;
@@ -116,20 +104,21 @@ __global__ __launch_bounds__(256) void k_pred_hidden(const void* __restrict__ p1
     for (int t = 0; t < NB; ++t) acc[t] = 0.f;
     for (int c0 = 0; c0 < nch; c0 += WAVE * U) {
       u32x4 w[U];
+      XChunk<PT, AT> xv[U][NB];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * WAVE + lane;
         w[u] = c < nch ? ld_stream(wrow + c) : u32x4{0, 0, 0, 0};
-      }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * WAVE + lane;
-        if (c < nch) {
-#pragma unroll
-          for (int t = 0; t < NB; ++t)
-            if (t0 + t < B) dot_chunk<PT, AT>(acc[t], w[u], xb + (size_t)(t0 + t) * d + (size_t)c * EPC, 1.f);
+        for (int t = 0; t < NB; ++t) {
+          if (c < nch && t0 + t < B) xv[u][t].load(xb + (size_t)(t0 + t) * d + (size_t)c * EPC);
+          else xv[u][t].zero();
         }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < NB; ++t) dot_chunk<PT, AT>(acc[t], w[u], xv[u][t], 1.f);
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
@@ -140,353 +129,412 @@ __global__ __launch_bounds__(256) void k_pred_hidden(const void* __restrict__ p1
 }
 
 // ---------------------------------------------------------------------------
-// a2/a4 + a3: v[t][i] = rows[i] . vec[t] + bias[i]; selected_i = OR_t v[t][i] > thr.
-// One workgroup (4 waves x 16 rows) per 64-row mask word; lane j of a wave
-// holds the decision for its row j and a ballot packs them.  The last
-// workgroup compacts all words into idx/count.
+// Partial dot products of RB rows against NB token vectors, per lane
+// (chunks c = lane, lane+64, ... of each row).  Rows with id < 0 are skipped.
 // ---------------------------------------------------------------------------
-template <int WT, int VT, int NB, int RG, int U>
-__global__ __launch_bounds__(256) void k_rows_mask(const void* __restrict__ rows, const f16* __restrict__ scales,
-                                                   const void* __restrict__ vec, int K, int n,
-                                                   const float* __restrict__ bias, float thr, int B,
-                                                   float* __restrict__ vals_out,
-                                                   unsigned long long* __restrict__ mask_words,
-                                                   unsigned* __restrict__ ticket, int* __restrict__ idx_out,
-                                                   int* __restrict__ count_out) {
-  using V = typename VecT<VT>::T;
-  constexpr int EPC = WFmt<WT>::EPC;
-  constexpr int RPW = 16;  // rows per wave
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int row_base = blockIdx.x * 64 + wave * RPW;
-  const int nch = K / EPC;
-  const V* vb = static_cast<const V*>(vec);
-  const char* rbase = static_cast<const char*>(rows);
-  const size_t rbytes = row_bytes(WT, (size_t)K);
-  bool dec = false;
-
-#pragma unroll 1
-  for (int rg = 0; rg < RPW; rg += RG) {
-    const u32x4* wr[RG];
-    const f16* sr[RG];
-#pragma unroll
-    for (int j = 0; j < RG; ++j) {
-      const int row = min(row_base + rg + j, n - 1);
-      wr[j] = reinterpret_cast<const u32x4*>(rbase + rbytes * row);
-      sr[j] = (WT == DT_Q4) ? scales + (size_t)row * (K / 32) : nullptr;
-    }
-    bool any[RG];
-#pragma unroll
-    for (int j = 0; j < RG; ++j) any[j] = false;
-    for (int t0 = 0; t0 < B; t0 += NB) {
-      float acc[RG][NB];
-#pragma unroll
-      for (int j = 0; j < RG; ++j)
-#pragma unroll
-        for (int t = 0; t < NB; ++t) acc[j][t] = 0.f;
-      for (int c0 = 0; c0 < nch; c0 += WAVE * U) {
-        u32x4 w[RG][U];
-        float sc[RG][U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = c0 + u * WAVE + lane;
-#pragma unroll
-          for (int j = 0; j < RG; ++j) {
-            w[j][u] = c < nch ? ld_stream(wr[j] + c) : u32x4{0, 0, 0, 0};
-            sc[j][u] = (WT == DT_Q4 && c < nch) ? (float)sr[j][c] : 1.f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = c0 + u * WAVE + lane;
-          if (c < nch) {
-#pragma unroll
-            for (int t = 0; t < NB; ++t) {
-              if (t0 + t < B) {
-                const V* vp = vb + (size_t)(t0 + t) * K + (size_t)c * EPC;
-#pragma unroll
-                for (int j = 0; j < RG; ++j) dot_chunk<WT, VT>(acc[j][t], w[j][u], vp, sc[j][u]);
-              }
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < RG; ++j) {
-        const int row = row_base + rg + j;
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          const float s = wave_sum(acc[j][t]);
-          if (row < n && t0 + t < B) {
-            const float v = s + bias[row];
-            if (vals_out != nullptr && lane == 0) vals_out[(size_t)(t0 + t) * n + row] = v;
-            any[j] = any[j] || (v > thr);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < RG; ++j)
-      if (lane == rg + j) dec = any[j];
-  }
-
-  __shared__ unsigned long long s_sub[4];
-  const unsigned long long bits = __ballot(dec) & 0xFFFFull;
-  if (lane == 0) s_sub[wave] = bits;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    mask_words[blockIdx.x] = s_sub[0] | (s_sub[1] << 16) | (s_sub[2] << 32) | (s_sub[3] << 48);
-  if (arrive_last(ticket, gridDim.x)) {
-    block_compact(mask_words, gridDim.x, idx_out, count_out);
-    if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// a5: row-gather GEMV over the selected neurons.  One wave per neuron,
-// persistent grid-stride over ranks k < count (count read on the device).
-//   GM_GATED        a = ReLU(W_gate[i].x + b_i) * (W_up[i].x)
-//   GM_NONGATED     a = ReLU(W_up[i].x + b_i)
-//   GM_EXACT_GATED  a = ReLU(g[i]) * (W_up[i].x)     (g from the dense pass)
-// a is stored by rank: a[t][k].
-// ---------------------------------------------------------------------------
-template <int WT, int AT, int NB, int GM, int U>
-__global__ __launch_bounds__(256) void k_gather(const void* __restrict__ w_gate, const void* __restrict__ w_up,
-                                                const f16* __restrict__ s_gate, const f16* __restrict__ s_up,
-                                                const float* __restrict__ bias, const float* __restrict__ g_ws,
-                                                const void* __restrict__ x, int d, int n, int B,
-                                                const int* __restrict__ idx, const int* __restrict__ count,
-                                                int dense, float* __restrict__ a_ws, int* __restrict__ iota_out,
-                                                int* __restrict__ count_out) {
-  using XT = typename VecT<AT>::T;
-  constexpr int EPC = WFmt<WT>::EPC;
-  constexpr bool TWO = (GM == GM_GATED);
+template <int RT, int VT, int NB, int RB, int U>
+__device__ __forceinline__ void rows_dot(float (&acc)[RB][NB], const char* __restrict__ rbase, size_t rbytes,
+                                         const f16* __restrict__ scales, int K, const int (&rows)[RB],
+                                         const typename VecT<VT>::T* __restrict__ vec, int t0, int B) {
+  constexpr int EPC = WFmt<RT>::EPC;
   const int lane = threadIdx.x & (WAVE - 1);
-  const int gw = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-  const int nw = gridDim.x * (blockDim.x / WAVE);
-  // A caller-given list is bounded here: count is clamped to [0, n] and
-  // entries outside [0, n) contribute nothing.
-  const int cnt = dense ? n : min(max(*count, 0), n);
-  const int nch = d / EPC;
-  const size_t rbytes = row_bytes(WT, (size_t)d);
-  const XT* xb = static_cast<const XT*>(x);
-  if (dense && count_out != nullptr && gw == 0 && lane == 0) *count_out = n;
-
-  for (int k = gw; k < cnt; k += nw) {
-    const int i = dense ? k : idx[k];
-    if (dense && iota_out != nullptr && lane == 0) iota_out[k] = k;
-    if ((unsigned)i >= (unsigned)n) {
-      if (lane == 0)
-        for (int t = 0; t < B; ++t) a_ws[(size_t)t * n + k] = 0.f;
-      continue;
-    }
-    const u32x4* ru = reinterpret_cast<const u32x4*>(static_cast<const char*>(w_up) + rbytes * i);
-    const u32x4* rg = TWO ? reinterpret_cast<const u32x4*>(static_cast<const char*>(w_gate) + rbytes * i) : nullptr;
-    const f16* su = (WT == DT_Q4) ? s_up + (size_t)i * (d / 32) : nullptr;
-    const f16* sg = (WT == DT_Q4 && TWO) ? s_gate + (size_t)i * (d / 32) : nullptr;
-    for (int t0 = 0; t0 < B; t0 += NB) {
-      float au[NB], ag[NB];
+  const int nch = K / EPC;
 #pragma unroll
-      for (int t = 0; t < NB; ++t) au[t] = ag[t] = 0.f;
-      for (int c0 = 0; c0 < nch; c0 += WAVE * U) {
-        u32x4 wu[U], wg[U];
-        float scu[U], scg[U];
+  for (int j = 0; j < RB; ++j)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = c0 + u * WAVE + lane;
-          const bool ok = c < nch;
-          wu[u] = ok ? ld_stream(ru + c) : u32x4{0, 0, 0, 0};
-          scu[u] = (WT == DT_Q4 && ok) ? (float)su[c] : 1.f;
-          if (TWO) {
-            wg[u] = ok ? ld_stream(rg + c) : u32x4{0, 0, 0, 0};
-            scg[u] = (WT == DT_Q4 && ok) ? (float)sg[c] : 1.f;
-          }
-        }
+    for (int t = 0; t < NB; ++t) acc[j][t] = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += WAVE * U) {
+    u32x4 w[RB][U];
+    float sc[RB][U];
+    XChunk<RT, VT> xv[U][NB];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = c0 + u * WAVE + lane;
-          if (c < nch) {
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * WAVE + lane;
 #pragma unroll
-            for (int t = 0; t < NB; ++t) {
-              if (t0 + t < B) {
-                const XT* xp = xb + (size_t)(t0 + t) * d + (size_t)c * EPC;
-                dot_chunk<WT, AT>(au[t], wu[u], xp, scu[u]);
-                if (TWO) dot_chunk<WT, AT>(ag[t], wg[u], xp, scg[u]);
-              }
-            }
-          }
-        }
+      for (int j = 0; j < RB; ++j) {
+        const bool ok = c < nch && rows[j] >= 0;
+        w[j][u] = ok ? ld_stream(reinterpret_cast<const u32x4*>(rbase + rbytes * rows[j]) + c) : u32x4{0, 0, 0, 0};
+        sc[j][u] = (RT == DT_Q4 && ok) ? (float)scales[(size_t)rows[j] * (K / 32) + c] : 1.f;
       }
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
-        const float su_ = wave_sum(au[t]);
-        float a;
-        if (GM == GM_GATED) {
-          const float sg_ = wave_sum(ag[t]);
-          a = fmaxf(sg_ + bias[i], 0.f) * su_;
-        } else if (GM == GM_NONGATED) {
-          a = fmaxf(su_ + bias[i], 0.f);
+        if (c < nch && t0 + t < B) xv[u][t].load(vec + (size_t)(t0 + t) * K + (size_t)c * EPC);
+        else xv[u][t].zero();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int j = 0; j < RB; ++j) dot_chunk<RT, VT>(acc[j][t], w[j][u], xv[u][t], sc[j][u]);
+  }
+}
+
+// Elements of one 16-byte weight chunk, as floats (q4: the group scale applied by the caller).
+template <int WT> struct Unpack;
+template <> struct Unpack<DT_F16> {
+  static constexpr int N = 8;
+  __device__ static void run(u32x4 w, float (&o)[8]) {
+    const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const f16x2 hh = as_h2(ws[p]);
+      o[2 * p] = (float)hh.x;
+      o[2 * p + 1] = (float)hh.y;
+    }
+  }
+};
+template <> struct Unpack<DT_F32> {
+  static constexpr int N = 4;
+  __device__ static void run(u32x4 w, float (&o)[4]) {
+    const f32x4 v = __builtin_bit_cast(f32x4, w);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+};
+template <> struct Unpack<DT_Q4> {
+  static constexpr int N = 32;
+  __device__ static void run(u32x4 w, float (&o)[32]) {
+    const unsigned ws[4] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u, w.z ^ 0x88888888u, w.w ^ 0x88888888u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const f16x2 qq = q4pair(ws[k] >> (8 * p));
+        o[8 * k + 2 * p] = (float)qq.x;
+        o[8 * k + 2 * p + 1] = (float)qq.y;
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// k_ffn_group: mask, gather, activation and the partial down projection of
+// one group of neurons (see the file header).
+// ---------------------------------------------------------------------------
+constexpr int kNWMax = 8;      // waves per group workgroup (4 or 8)
+constexpr int kGMax = 128;     // largest group
+
+// Selected neurons per gather batch: the batch's gate/up/down pieces are all in flight at once.
+template <int WT, int CPL> struct Batch { static constexpr int JB = ((WT == DT_Q4) ? 4 : 8) / CPL > 0 ? ((WT == DT_Q4) ? 4 : 8) / CPL : 1; };
+constexpr int kJBMax = 8;
+
+template <int WT, int AT, int NB, int MODE, int CPL, int NW>
+__global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
+  using XT = typename VecT<AT>::T;
+  constexpr int EPC = WFmt<WT>::EPC;
+  constexpr int NE = Unpack<WT>::N;
+  constexpr int kJB = Batch<WT, CPL>::JB;
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int G = A.G, B = A.B, d = A.d, n = A.n;
+  const int grp = blockIdx.x;
+  const int g0 = grp * G;
+  const XT* xb = static_cast<const XT*>(A.x);
+
+  __shared__ unsigned s_mask[kGMax / 32];
+  __shared__ int s_list[kGMax];
+  __shared__ int s_m;
+  __shared__ float s_bias[kGMax];    // b of the group's neurons
+  __shared__ float s_bpre[kGMax];    // b_p (predictor) of the group's neurons
+  __shared__ float s_g[(MODE == MODE_EXACT) ? kGMax * kMaxTokens : 1];
+  __shared__ float s_part[kJBMax][2][NB][NW];
+  __shared__ float s_a[kJBMax][NB];
+
+  // biases of the group's own neurons, fetched once up front
+  if (MODE != MODE_LIST && (int)threadIdx.x < G) {
+    const int i = g0 + threadIdx.x;
+    s_bias[threadIdx.x] = i < n ? A.b[i] : 0.f;
+    if (MODE == MODE_PRED) s_bpre[threadIdx.x] = i < n ? A.b_p[i] : 0.f;
+  }
+
+  // ---- which neurons of the group are computed ------------------------------------------------
+  if (MODE == MODE_PRED || MODE == MODE_EXACT) {
+    if (threadIdx.x < kGMax / 32) s_mask[threadIdx.x] = 0u;
+    __syncthreads();
+    const int rpw = G / NW;   // rows per wave, <= 32
+    constexpr int RB = (MODE == MODE_PRED) ? 8 : 4;
+    bool dec = false;
+#pragma unroll 1
+    for (int rb = 0; rb < rpw; rb += RB) {
+      int rows[RB];
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const int row = g0 + wave * rpw + rb + j;
+        rows[j] = (rb + j < rpw && row < n) ? row : -1;
+      }
+      bool any[RB];
+#pragma unroll
+      for (int j = 0; j < RB; ++j) any[j] = false;
+      for (int t0 = 0; t0 < B; t0 += NB) {
+        float acc[RB][NB];
+        if (MODE == MODE_PRED) {
+          if (A.p_dtype == DT_F16)
+            rows_dot<DT_F16, DT_F32, NB, RB, 2>(acc, static_cast<const char*>(A.p2), row_bytes(DT_F16, A.r), nullptr,
+                                                 A.r, rows, A.h, t0, B);
+          else
+            rows_dot<DT_F32, DT_F32, NB, RB, 2>(acc, static_cast<const char*>(A.p2), row_bytes(DT_F32, A.r), nullptr,
+                                                 A.r, rows, A.h, t0, B);
         } else {
-          a = fmaxf(g_ws[(size_t)(t0 + t) * n + i], 0.f) * su_;
+          const void* wpre = A.gated ? A.w_gate : A.w_up;
+          const f16* spre = A.gated ? A.s_gate : A.s_up;
+          rows_dot<WT, AT, NB, RB, 4>(acc, static_cast<const char*>(wpre), row_bytes(WT, d), spre, d, rows, xb, t0, B);
         }
-        if (lane == 0 && t0 + t < B) a_ws[(size_t)(t0 + t) * n + k] = a;
+        const float* bias = (MODE == MODE_PRED) ? s_bpre : s_bias;
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+#pragma unroll
+          for (int t = 0; t < NB; ++t) {
+            const float v = wave_sum(acc[j][t]) + (rows[j] >= 0 ? bias[wave * rpw + rb + j] : 0.f);
+            if (rows[j] >= 0 && t0 + t < B) {
+              if (MODE == MODE_PRED && A.logits != nullptr && lane == 0) A.logits[(size_t)(t0 + t) * n + rows[j]] = v;
+              if (MODE == MODE_EXACT && lane == 0) s_g[(wave * rpw + rb + j) * kMaxTokens + t0 + t] = v;
+              any[j] = any[j] || (v > A.thr);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < RB; ++j)
+        if (lane == rb + j) dec = any[j];
+    }
+    // lane j of the wave holds row (wave * rpw + j); place the wave's bits in the group's words
+    const unsigned long long bits = __ballot(dec) & ((1ull << rpw) - 1ull);
+    if (lane == 0 && bits) {
+      const int bit0 = wave * rpw;
+      atomicOr(&s_mask[bit0 / 32], (unsigned)(bits << (bit0 % 32)));
+      if (bit0 % 32 + rpw > 32) atomicOr(&s_mask[bit0 / 32 + 1], (unsigned)(bits >> (32 - bit0 % 32)));
+    }
+    __syncthreads();
+    const int n_gw = G / 32;
+    if ((int)threadIdx.x < n_gw && g0 / 32 + (int)threadIdx.x < (n + 31) / 32)
+      A.mask_words[g0 / 32 + threadIdx.x] = s_mask[threadIdx.x];
+    if ((int)threadIdx.x < G) {
+      const int q = threadIdx.x / 32, bit = threadIdx.x % 32;
+      const unsigned word = s_mask[q];
+      int pos = __popc(word & ((1u << bit) - 1u));
+      for (int qq = 0; qq < q; ++qq) pos += __popc(s_mask[qq]);
+      if ((word >> bit) & 1u) s_list[pos] = threadIdx.x;
+    }
+    if (threadIdx.x == 0) {
+      int m = 0;
+      for (int q = 0; q < n_gw; ++q) m += __popc(s_mask[q]);
+      s_m = m;
+    }
+  } else if (MODE == MODE_DENSE) {
+    const int m = max(0, min(G, n - g0));
+    if ((int)threadIdx.x < G) s_list[threadIdx.x] = threadIdx.x;
+    if (threadIdx.x == 0) s_m = m;
+  } else {  // MODE_LIST: an even slice of the caller's list per workgroup
+    const int cnt = min(max(*A.list_count, 0), n);
+    const int per = (cnt + (int)gridDim.x - 1) / (int)gridDim.x;   // <= G since gridDim.x = ceil(n / G)
+    const int e0 = grp * per;
+    const int m = max(0, min(per, cnt - e0));
+    if ((int)threadIdx.x < m) {
+      const int id = A.list[e0 + threadIdx.x];
+      s_list[threadIdx.x] = ((unsigned)id < (unsigned)n) ? id : -1;
+    }
+    if (threadIdx.x == 0) s_m = m;
+  }
+  __syncthreads();
+  if (A.mask_only) return;
+  const int m = s_m;
+
+  // ---- this wave's d-slice -------------------------------------------------------------------
+  const int nch = d / EPC;
+  const int cpw = (nch + NW - 1) / NW;
+  const int c_begin = wave * cpw, c_end = min(nch, c_begin + cpw);
+  const size_t rbytes = row_bytes(WT, d);
+  const char* wgb = static_cast<const char*>(A.w_gate);
+  const char* wub = static_cast<const char*>(A.w_up);
+  const char* wdb = static_cast<const char*>(A.w_down_t);
+  const bool need_gate = A.gated && MODE != MODE_EXACT;
+  const bool need_up = !(MODE == MODE_EXACT && !A.gated);
+
+  for (int t0 = 0; t0 < B; t0 += NB) {
+    float acc[CPL][NB][NE];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q)
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[q][t][e] = 0.f;
+
+    XChunk<WT, AT> xq[CPL][NB];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int c = c_begin + lane + q * WAVE;
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        if (c < c_end && t0 + t < B) xq[q][t].load(xb + (size_t)(t0 + t) * d + (size_t)c * EPC);
+        else xq[q][t].zero();
+      }
+    }
+
+    for (int j0 = 0; j0 < m; j0 += kJB) {
+      int nid[kJB];
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj) {
+        const int j = j0 + jj;
+        int id = -1;
+        if (j < m) id = (MODE == MODE_LIST) ? s_list[j] : g0 + s_list[j];
+        nid[jj] = id;
+      }
+      // issue every load of the batch: gate, up and down pieces of this wave's slice
+      u32x4 wg[kJB][CPL], wu[kJB][CPL], wd[kJB][CPL];
+      float sg[kJB][CPL], su[kJB][CPL], sd[kJB][CPL];
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj)
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          const int c = c_begin + lane + q * WAVE;
+          const bool ok = nid[jj] >= 0 && c < c_end;
+          const size_t off = rbytes * (size_t)(ok ? nid[jj] : 0);
+          const size_t soff = (size_t)(ok ? nid[jj] : 0) * (d / 32) + c;
+          wg[jj][q] = (ok && need_gate) ? ld_stream(reinterpret_cast<const u32x4*>(wgb + off) + c) : u32x4{0, 0, 0, 0};
+          wu[jj][q] = (ok && need_up) ? ld_stream(reinterpret_cast<const u32x4*>(wub + off) + c) : u32x4{0, 0, 0, 0};
+          wd[jj][q] = ok ? ld_stream(reinterpret_cast<const u32x4*>(wdb + off) + c) : u32x4{0, 0, 0, 0};
+          sg[jj][q] = (WT == DT_Q4 && ok && need_gate) ? (float)A.s_gate[soff] : 1.f;
+          su[jj][q] = (WT == DT_Q4 && ok && need_up) ? (float)A.s_up[soff] : 1.f;
+          sd[jj][q] = (WT == DT_Q4 && ok) ? (float)A.s_down[soff] : 1.f;
+        }
+      // partial dot products over the slice, folded across the wave
+      if (need_gate || need_up) {
+#pragma unroll
+        for (int jj = 0; jj < kJB; ++jj) {
+          float pg[NB], pu[NB];
+#pragma unroll
+          for (int t = 0; t < NB; ++t) pg[t] = pu[t] = 0.f;
+#pragma unroll
+          for (int q = 0; q < CPL; ++q) {
+            const int c = c_begin + lane + q * WAVE;
+            if (nid[jj] >= 0 && c < c_end) {
+#pragma unroll
+              for (int t = 0; t < NB; ++t) {
+                if (need_gate) dot_chunk<WT, AT>(pg[t], wg[jj][q], xq[q][t], sg[jj][q]);
+                if (need_up) dot_chunk<WT, AT>(pu[t], wu[jj][q], xq[q][t], su[jj][q]);
+              }
+            }
+          }
+          if (j0 + jj < m) {
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+              const float vg = need_gate ? wave_sum(pg[t]) : 0.f;
+              const float vu = wave_sum(pu[t]);
+              if (lane == 0) {
+                s_part[jj][0][t][wave] = vg;
+                s_part[jj][1][t][wave] = vu;
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < kJB * NB) {
+        const int jj = threadIdx.x / NB, t = threadIdx.x % NB;
+        float a = 0.f;
+        if (j0 + jj < m && nid[jj] >= 0 && t0 + t < B) {
+          float sg_ = 0.f, su_ = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            sg_ += s_part[jj][0][t][w];
+            su_ += s_part[jj][1][t][w];
+          }
+          if (MODE == MODE_EXACT) {
+            const float g = s_g[s_list[j0 + jj] * kMaxTokens + t0 + t];
+            a = A.gated ? fmaxf(g, 0.f) * su_ : fmaxf(g, 0.f);
+          } else {
+            const float bj = (MODE == MODE_LIST) ? A.b[nid[jj]] : s_bias[s_list[j0 + jj]];
+            a = A.gated ? fmaxf(sg_ + bj, 0.f) * su_ : fmaxf(su_ + bj, 0.f);
+          }
+        }
+        s_a[jj][t] = a;
+      }
+      __syncthreads();
+      // down: acc[slice] += a_j * W_downT[j][slice]
+#pragma unroll
+      for (int jj = 0; jj < kJB; ++jj) {
+        if (j0 + jj < m) {
+#pragma unroll
+          for (int q = 0; q < CPL; ++q) {
+            float wf[NE];
+            Unpack<WT>::run(wd[jj][q], wf);
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+              const float as = s_a[jj][t] * sd[jj][q];
+#pragma unroll
+              for (int e = 0; e < NE; ++e) acc[q][t][e] = fmaf(as, wf[e], acc[q][t][e]);
+            }
+          }
+        }
+      }
+    }
+    // the group's partial of y for this wave's slice (zeros if nothing was selected)
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int c = c_begin + lane + q * WAVE;
+      if (c < c_end) {
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          if (t0 + t < B) {
+            float* dst = A.partial + ((size_t)grp * B + t0 + t) * d + (size_t)c * EPC;
+#pragma unroll
+            for (int e = 0; e < NE; e += 4)
+              *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[q][t][e], acc[q][t][e + 1], acc[q][t][e + 2], acc[q][t][e + 3]};
+          }
+        }
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// a6 + a7: y[t] = sum over ranks k < count of a[t][k] * W_downT[idx[k]].
-// Workgroup (tile, s) owns output columns [tile*TW, (tile+1)*TW) and the ranks
-// k = s*4 + wave (mod 4*S).  Waves fold into the workgroup's partial through
-// LDS; the last of the S workgroups of a tile sums the S partials in order
-// s = 0..S-1 and writes y.
-//   ASRC_A      a[t][k] from the gather pass
-//   ASRC_GRELU  a[t][k] = ReLU(g[t][idx[k]])      (non-gated exact mode: u = 1)
+// k_finish: y[t][c] = sum over groups g (in order) of partial[g][t][c]; the
+// extra last workgroup writes the index list (compacted mask words, or 0..n-1).
 // ---------------------------------------------------------------------------
-template <int WT> struct DownFmt;
-template <> struct DownFmt<DT_F32> { static constexpr int EPL = 4; };
-template <> struct DownFmt<DT_F16> { static constexpr int EPL = 8; };
-template <> struct DownFmt<DT_Q4> { static constexpr int EPL = 16; };
-
-template <int WT, int OT, int NB, int ASRC, int U>
-__global__ __launch_bounds__(256) void k_down(const void* __restrict__ w_down_t, const f16* __restrict__ s_down,
-                                              const float* __restrict__ a_ws, const float* __restrict__ g_ws,
-                                              int d, int n, int B, const int* __restrict__ idx,
-                                              const int* __restrict__ count, int dense, int S,
-                                              float* __restrict__ partial, unsigned* __restrict__ tickets,
-                                              void* __restrict__ y) {
+template <int OT>
+__global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partial, int NG, int B, int d,
+                                                void* __restrict__ y, const unsigned* __restrict__ mask_words,
+                                                int n_words, int iota_n, int* __restrict__ idx_out,
+                                                int* __restrict__ count_out, int n_col_blocks) {
   using YT = typename VecT<OT>::T;
-  constexpr int EPL = DownFmt<WT>::EPL;
-  constexpr int TW = WAVE * EPL;
-  extern __shared__ float s_red[];  // [4][NB][TW]
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int tile = blockIdx.x, s = blockIdx.y;
-  const int col0 = tile * TW + lane * EPL;
-  const bool col_ok = col0 < d;
-  const int cnt = dense ? n : min(max(*count, 0), n);
-  const int stride = S * 4;
-  const size_t rbytes = row_bytes(WT, (size_t)d);
-  const char* wb = static_cast<const char*>(w_down_t);
-
-  for (int t0 = 0; t0 < B; t0 += NB) {
-    float acc[NB][EPL];
-#pragma unroll
-    for (int t = 0; t < NB; ++t)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
-
-    for (int k0 = s * 4 + wave; k0 < cnt; k0 += stride * U) {
-      int ii[U];
-      float av[U][NB];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + u * stride;
-        int i = k < cnt ? (dense ? k : idx[k]) : -1;
-        if ((unsigned)i >= (unsigned)n) i = -1;
-        const bool ok = i >= 0;
-        ii[u] = i;
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          float a = 0.f;
-          if (ok && t0 + t < B) {
-            if (ASRC == ASRC_A) a = a_ws[(size_t)(t0 + t) * n + k];
-            else a = fmaxf(g_ws[(size_t)(t0 + t) * n + ii[u]], 0.f);
-          }
-          av[u][t] = a;
-        }
-      }
-      if (WT == DT_Q4) {
-        u32x2 q[U];
-        float sc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const bool ok = ii[u] >= 0 && col_ok;
-          const char* rp = wb + rbytes * (ok ? ii[u] : 0);
-          q[u] = ok ? ld_stream(reinterpret_cast<const u32x2*>(rp + col0 / 2)) : u32x2{0u, 0u};
-          sc[u] = ok ? (float)s_down[(size_t)ii[u] * (d / 32) + col0 / 32] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float qf[16];
-          const unsigned wds[2] = {q[u].x ^ 0x88888888u, q[u].y ^ 0x88888888u};
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const f16x2 qq = q4pair(wds[kk] >> (8 * p));
-              qf[kk * 8 + 2 * p] = (float)qq.x;
-              qf[kk * 8 + 2 * p + 1] = (float)qq.y;
-            }
-#pragma unroll
-          for (int t = 0; t < NB; ++t) {
-            const float as = av[u][t] * sc[u];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[t][e] = fmaf(as, qf[e], acc[t][e]);
-          }
-        }
-      } else {
-        u32x4 w[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const bool ok = ii[u] >= 0 && col_ok;
-          const char* rp = wb + rbytes * (ok ? ii[u] : 0);
-          w[u] = ok ? ld_stream(reinterpret_cast<const u32x4*>(rp + row_bytes(WT, (size_t)col0)))
-                    : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float wf[EPL];
-          if (WT == DT_F16) {
-            const unsigned ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const f16x2 hh = as_h2(ws[p]);
-              wf[2 * p] = (float)hh.x;
-              wf[2 * p + 1] = (float)hh.y;
-            }
-          } else {
-            const f32x4 v = __builtin_bit_cast(f32x4, w[u]);
-            wf[0] = v.x; wf[1] = v.y; wf[2] = v.z; wf[3] = v.w;
-          }
-#pragma unroll
-          for (int t = 0; t < NB; ++t)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[t][e] = fmaf(av[u][t], wf[e], acc[t][e]);
-        }
-      }
+  if ((int)blockIdx.x == n_col_blocks) {
+    if (mask_words != nullptr) {
+      block_compact(mask_words, n_words, idx_out, count_out);
+    } else if (iota_n > 0) {
+      for (int i = threadIdx.x; i < iota_n; i += blockDim.x) idx_out[i] = i;
+      if (threadIdx.x == 0) *count_out = iota_n;
     }
-
-    // fold the 4 waves: wave w writes its columns, then each thread sums 4 values in order
-#pragma unroll
-    for (int t = 0; t < NB; ++t)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_red[(wave * NB + t) * TW + lane * EPL + e] = acc[t][e];
-    __syncthreads();
-    for (int e = threadIdx.x; e < NB * TW; e += blockDim.x) {
-      const int t = e / TW, j = e % TW;
-      const int col = tile * TW + j;
-      if (t0 + t < B && col < d) {
-        const float v = ((s_red[(0 * NB + t) * TW + j] + s_red[(1 * NB + t) * TW + j]) +
-                         s_red[(2 * NB + t) * TW + j]) + s_red[(3 * NB + t) * TW + j];
-        partial[((size_t)s * B + t0 + t) * d + col] = v;
-      }
-    }
-    __syncthreads();
+    return;
   }
-
-  if (arrive_last(tickets + tile, (unsigned)S)) {
-    YT* yo = static_cast<YT*>(y);
-    for (int e = threadIdx.x; e < B * TW; e += blockDim.x) {
-      const int t = e / TW, j = e % TW;
-      const int col = tile * TW + j;
-      if (col >= d) continue;
-      float sum = 0.f;
-      for (int s2 = 0; s2 < S; ++s2)
-        sum += __hip_atomic_load(partial + ((size_t)s2 * B + t) * d + col, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      yo[(size_t)t * d + col] = from_f32<YT>(sum);
+  // 256 threads = 16 column quads (64 columns) x 16 slices of the groups
+  __shared__ f32x4 s_red[16][16];
+  const int cq = threadIdx.x % 16, q = threadIdx.x / 16;
+  const int col = blockIdx.x * 64 + cq * 4;
+  YT* yo = static_cast<YT*>(y);
+  for (int t = 0; t < B; ++t) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    if (col < d) {
+      for (int g0 = q; g0 < NG; g0 += 16 * 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int g = g0 + 16 * u;
+          v[u] = g < NG ? *reinterpret_cast<const f32x4*>(partial + ((size_t)g * B + t) * d + col)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+      }
     }
-    if (threadIdx.x == 0) __hip_atomic_store(tickets + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_red[q][cq] = sum;
+    __syncthreads();
+    if (q == 0 && col < d) {
+      f32x4 tot = s_red[0][cq];
+#pragma unroll
+      for (int k = 1; k < 16; ++k) tot += s_red[k][cq];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yo[(size_t)t * d + col + e] = from_f32<YT>(tot[e]);
+    }
+    __syncthreads();
   }
 }
 
@@ -503,8 +551,11 @@ hipError_t with_nb(int B, F&& f) {
 }
 }  // namespace
 
-int down_tile_width(int wt) {
-  return WAVE * (wt == DT_F32 ? DownFmt<DT_F32>::EPL : (wt == DT_F16 ? DownFmt<DT_F16>::EPL : DownFmt<DT_Q4>::EPL));
+int group_cpl(int wt, int d, int nw) {
+  const int epc = wt == DT_F32 ? 4 : (wt == DT_F16 ? 8 : 32);
+  const int nch = d / epc;
+  const int cpw = (nch + nw - 1) / nw;
+  return cpw <= 64 ? 1 : (cpw <= 128 ? 2 : (cpw <= 256 ? 4 : 0));
 }
 
 hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t s) {
@@ -533,90 +584,61 @@ hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int
   });
 }
 
-hipError_t launch_rows_mask(int wt, int vt, const void* rows, const void* scales, const void* vec, int K, int n,
-                            const float* bias, float thr, int B, float* vals_out,
-                            unsigned long long* mask_words, unsigned* ticket, int* idx_out, int* count_out,
-                            hipStream_t s) {
-  const int n_words = (n + 63) / 64;
-  const dim3 grid(n_words), block(kBlock);
-  const f16* sc = static_cast<const f16*>(scales);
-  return with_nb(B, [&](auto nbc) -> hipError_t {
+hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s) {
+  const int ng = (a.n + a.G - 1) / a.G;
+  if (a.G % 32 != 0 || a.G > kGMax || (a.nw != 4 && a.nw != 8) || a.G / a.nw > 32) return hipErrorInvalidValue;
+  const dim3 grid(ng), block(a.nw * WAVE);
+  const int cpl = group_cpl(wt, a.d, a.nw);
+  if (cpl == 0) return hipErrorInvalidValue;
+  return with_nb(a.B, [&](auto nbc) -> hipError_t {
     constexpr int NB = decltype(nbc)::value;
-    constexpr int RG = 4, U = 4;
-#define PIK_ROWS_MASK(W, V)                                                                                  \
-  hipLaunchKernelGGL((k_rows_mask<W, V, NB, RG, U>), grid, block, 0, s, rows, sc, vec, K, n, bias, thr, B, \
-                     vals_out, mask_words, ticket, idx_out, count_out)
-    if (wt == DT_F16 && vt == DT_F16) PIK_ROWS_MASK(DT_F16, DT_F16);
-    else if (wt == DT_F16 && vt == DT_F32) PIK_ROWS_MASK(DT_F16, DT_F32);
-    else if (wt == DT_F32 && vt == DT_F32) PIK_ROWS_MASK(DT_F32, DT_F32);
-    else if (wt == DT_F32 && vt == DT_F16) PIK_ROWS_MASK(DT_F32, DT_F16);
-    else if (wt == DT_Q4 && vt == DT_F16) PIK_ROWS_MASK(DT_Q4, DT_F16);
-    else if (wt == DT_Q4 && vt == DT_F32) PIK_ROWS_MASK(DT_Q4, DT_F32);
+#define PIK_GRP(W, AC, M, C, NWV) hipLaunchKernelGGL((k_ffn_group<W, AC, NB, M, C, NWV>), grid, block, 0, s, a)
+#define PIK_GRP_NW(W, AC, M, C)                 \
+  do {                                          \
+    if (a.nw == 4) PIK_GRP(W, AC, M, C, 4);     \
+    else PIK_GRP(W, AC, M, C, 8);               \
+  } while (0)
+#define PIK_GRP_C(W, AC, M)                      \
+  do {                                           \
+    if (cpl == 1) PIK_GRP_NW(W, AC, M, 1);       \
+    else if (cpl == 2) PIK_GRP_NW(W, AC, M, 2);  \
+    else PIK_GRP_NW(W, AC, M, 4);                \
+  } while (0)
+#define PIK_GRP_M(W, AC)                                       \
+  do {                                                         \
+    if (mode == MODE_PRED) PIK_GRP_C(W, AC, MODE_PRED);        \
+    else if (mode == MODE_EXACT) PIK_GRP_C(W, AC, MODE_EXACT); \
+    else if (mode == MODE_DENSE) PIK_GRP_C(W, AC, MODE_DENSE); \
+    else PIK_GRP_C(W, AC, MODE_LIST);                          \
+  } while (0)
+    if (wt == DT_F16 && at == DT_F16) PIK_GRP_M(DT_F16, DT_F16);
+    else if (wt == DT_F16 && at == DT_F32) PIK_GRP_M(DT_F16, DT_F32);
+    else if (wt == DT_F32 && at == DT_F32) PIK_GRP_M(DT_F32, DT_F32);
+    else if (wt == DT_F32 && at == DT_F16) PIK_GRP_M(DT_F32, DT_F16);
+    else if (wt == DT_Q4 && at == DT_F16) PIK_GRP_M(DT_Q4, DT_F16);
+    else if (wt == DT_Q4 && at == DT_F32) PIK_GRP_M(DT_Q4, DT_F32);
     else return hipErrorInvalidValue;
-#undef PIK_ROWS_MASK
+#undef PIK_GRP_M
+#undef PIK_GRP_C
+#undef PIK_GRP_NW
+#undef PIK_GRP
     return hipGetLastError();
   });
 }
 
-hipError_t launch_gather(int wt, int at, int gm, const void* w_gate, const void* w_up, const void* s_gate,
-                         const void* s_up, const float* bias, const float* g_ws, const void* x, int d, int n,
-                         int B, const int* idx, const int* count, int dense, float* a_ws, int* iota_out,
-                         int* count_out, int grid_blocks, hipStream_t s) {
-  const dim3 grid(grid_blocks), block(kBlock);
-  const f16* sg = static_cast<const f16*>(s_gate);
-  const f16* su = static_cast<const f16*>(s_up);
-  return with_nb(B, [&](auto nbc) -> hipError_t {
-    constexpr int NB = decltype(nbc)::value;
-#define PIK_GATHER_GM(W, A, G, U)                                                                                \
-  hipLaunchKernelGGL((k_gather<W, A, NB, G, U>), grid, block, 0, s, w_gate, w_up, sg, su, bias, g_ws, x, d, n, B, \
-                     idx, count, dense, a_ws, iota_out, count_out)
-#define PIK_GATHER(W, A, U)                                              \
-  do {                                                                   \
-    if (gm == GM_GATED) PIK_GATHER_GM(W, A, GM_GATED, U);                \
-    else if (gm == GM_NONGATED) PIK_GATHER_GM(W, A, GM_NONGATED, U);     \
-    else PIK_GATHER_GM(W, A, GM_EXACT_GATED, U);                         \
-  } while (0)
-    if (wt == DT_F16 && at == DT_F16) PIK_GATHER(DT_F16, DT_F16, 8);
-    else if (wt == DT_F16 && at == DT_F32) PIK_GATHER(DT_F16, DT_F32, 8);
-    else if (wt == DT_F32 && at == DT_F32) PIK_GATHER(DT_F32, DT_F32, 8);
-    else if (wt == DT_F32 && at == DT_F16) PIK_GATHER(DT_F32, DT_F16, 8);
-    else if (wt == DT_Q4 && at == DT_F16) PIK_GATHER(DT_Q4, DT_F16, 4);
-    else if (wt == DT_Q4 && at == DT_F32) PIK_GATHER(DT_Q4, DT_F32, 4);
-    else return hipErrorInvalidValue;
-#undef PIK_GATHER
-#undef PIK_GATHER_GM
-    return hipGetLastError();
-  });
-}
-
-hipError_t launch_down(int wt, int ot, int asrc, const void* w_down_t, const void* s_down, const float* a_ws,
-                       const float* g_ws, int d, int n, int B, const int* idx, const int* count, int dense, int S,
-                       float* partial, unsigned* tickets, void* y, hipStream_t s) {
-  const int tw = down_tile_width(wt);
-  const dim3 grid((d + tw - 1) / tw, S), block(kBlock);
-  const f16* sd = static_cast<const f16*>(s_down);
-  return with_nb(B, [&](auto nbc) -> hipError_t {
-    constexpr int NB = decltype(nbc)::value;
-    const size_t lds = sizeof(float) * 4 * NB * tw;
-#define PIK_DOWN_A(W, O, A)                                                                                    \
-  hipLaunchKernelGGL((k_down<W, O, NB, A, 4>), grid, block, lds, s, w_down_t, sd, a_ws, g_ws, d, n, B, idx, count, \
-                     dense, S, partial, tickets, y)
-#define PIK_DOWN(W, O)                                   \
-  do {                                                   \
-    if (asrc == ASRC_A) PIK_DOWN_A(W, O, ASRC_A);        \
-    else PIK_DOWN_A(W, O, ASRC_GRELU);                   \
-  } while (0)
-    if (wt == DT_F16 && ot == DT_F16) PIK_DOWN(DT_F16, DT_F16);
-    else if (wt == DT_F16 && ot == DT_F32) PIK_DOWN(DT_F16, DT_F32);
-    else if (wt == DT_F32 && ot == DT_F32) PIK_DOWN(DT_F32, DT_F32);
-    else if (wt == DT_F32 && ot == DT_F16) PIK_DOWN(DT_F32, DT_F16);
-    else if (wt == DT_Q4 && ot == DT_F16) PIK_DOWN(DT_Q4, DT_F16);
-    else if (wt == DT_Q4 && ot == DT_F32) PIK_DOWN(DT_Q4, DT_F32);
-    else return hipErrorInvalidValue;
-#undef PIK_DOWN
-#undef PIK_DOWN_A
-    return hipGetLastError();
-  });
+hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
+                         const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,
+                         bool reduce, bool index_list, hipStream_t s) {
+  const int ncol = reduce ? (d + 63) / 64 : 0;
+  const int grid = ncol + (index_list ? 1 : 0);
+  if (grid == 0) return hipSuccess;
+  if (ot == DT_F16)
+    hipLaunchKernelGGL((k_finish<DT_F16>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
+                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
+  else
+    hipLaunchKernelGGL((k_finish<DT_F32>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
+                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
+  return hipGetLastError();
 }
 
 }  // namespace pik

@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the activation-sparse ReLU FFN decode step on one MI355X.
+
+One step = one decode token through all L distinct layers of the workload
+(every layer's weights resident in HBM; walking all L layers per token keeps
+the 256 MB Infinity Cache from serving repeats).  Each token's L-layer chain is
+captured once as a HIP graph and replayed; HIP events bracket exactly --steps
+replays.  Reported value: layers/s.  Also reported: effective HBM GB/s on the
+step's algorithmic bytes, the FFN-only tokens/s equivalent, a per-kernel
+breakdown measured with HIP events around each kernel, the roofline of the
+dominant kernel, and the CPU oracle timed on a bounded sample on the host.
+
+    python bench.py [--config llama7b] [--mode predicted] [--batch 1] [--steps K] [--warmup W]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "sparse-FFN decode layers/s + effective HBM GB/s on active-neuron bytes"
+PHASES_BY_MODE = {
+    "predicted": ("pred_hidden", "group", "finish"),
+    "exact": ("group", "finish"),
+    "dense": ("group", "finish"),
+}
+
+
+def esize(dt: str) -> float:
+    return {"f32": 4.0, "f16": 2.0}[dt]
+
+
+def row_bytes(dt: str, k: int) -> float:
+    if dt == "q4g32":
+        return k / 2 + (k / 32) * 2          # nibbles + fp16 group scales
+    return k * esize(dt)
+
+
+def step_bytes(cfg, mode: str, B: int, count: int) -> float:
+    """Algorithmic bytes of one layer-step: what the method must move.
+
+    Predictor weights and bias (predicted mode), the dense pre-activation
+    matrix and bias (exact mode), the selected neurons' rows of every matrix
+    the mode touches (q4 scales included) and their fp32 bias, x, y and the
+    index list.  Split partials and other scratch traffic are excluded.
+    """
+    d, n, r = cfg.d_model, cfg.d_ffn, cfg.rank
+    ea, rb = esize(cfg.act_dtype), row_bytes(cfg.w_dtype, d)
+    io = 2 * B * d * ea + 4 * count
+    if mode == "predicted":
+        pred = (r * d + n * r) * esize(cfg.p_dtype) + 4 * n
+        rows = (3 if cfg.gated else 2) * rb
+        return pred + count * (rows + 4) + io
+    if mode == "exact":
+        pre = n * rb + 4 * n
+        rows = (2 if cfg.gated else 1) * rb     # up (gated) + down; the pre-activation matrix was read densely
+        return pre + count * rows + io
+    rows = (3 if cfg.gated else 2) * rb
+    return count * (rows + 4) + io
+
+
+def phase_bytes(cfg, mode: str, phase: str, B: int, count: int) -> float:
+    """Algorithmic bytes one launch of a phase's kernel moves.
+
+    pred_hidden: P1, x, h.  group: the mask source (P2 + b_p, or the dense
+    pre-activation rows + b), the selected rows of every matrix the mode reads
+    with their bias, x and the mask bits; its partial-sum writes are scratch
+    and not counted.  finish: y and the index list.
+    """
+    d, n, r = cfg.d_model, cfg.d_ffn, cfg.rank
+    ea, rb = esize(cfg.act_dtype), row_bytes(cfg.w_dtype, d)
+    if phase == "pred_hidden":
+        return r * d * esize(cfg.p_dtype) + B * d * ea + B * r * 4
+    if phase == "group":
+        xb = B * d * ea + n / 8
+        if mode == "predicted":
+            return n * r * esize(cfg.p_dtype) + 4 * n + B * r * 4 + count * ((3 if cfg.gated else 2) * rb + 4) + xb
+        if mode == "exact":
+            return n * rb + 4 * n + count * ((2 if cfg.gated else 1) * rb) + xb
+        return count * ((3 if cfg.gated else 2) * rb + 4) + xb
+    if phase == "finish":
+        return B * d * ea + 4 * count
+    raise KeyError(phase)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "activation_sparse_decode_relu_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_phase: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernels."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(f"{workload}/{kernel_phase}")
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, mode: str, B: int, host_layers: dict, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    from synth import make_tokens
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = len(os.sched_getaffinity(0))
+    done, elapsed = 0, 0.0
+    per_layer = budget_s / max(1, len(host_layers))
+    for l, layer in host_layers.items():
+        # decode the stored weights once per layer, outside the timed region
+        weights = (oracle.dense_weights(layer.w_gate, layer.s_gate) if layer.gated else None,
+                   oracle.dense_weights(layer.w_up, layer.s_up), oracle.dense_weights(layer.w_down_t, layer.s_down))
+        x = make_tokens(cfg, l, 16 * B)
+        spent = 0.0
+        for t in range(16):
+            t0 = time.perf_counter()
+            oracle.forward(layer, x[t * B:(t + 1) * B], mode, weights=weights)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent > per_layer:
+                break
+        elapsed += spent
+        del weights
+    return {"value": done / elapsed if elapsed > 0 else None, "unit": "layers/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{done} layer-steps (batch {B}, {mode}) on layers {sorted(host_layers)}; float64 numpy, "
+                      f"weights decoded outside the timed region; {elapsed:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed steps (one step = one token through all layers)")
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="llama7b")
+    ap.add_argument("--mode", default="predicted", choices=("predicted", "exact", "dense"))
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--tokens", type=int, default=64, help="distinct token inputs per layer, replayed round-robin")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's own)")
+    ap.add_argument("--profile-tokens", type=int, default=4, help="tokens of the per-kernel event pass")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the sparse FFN path here runs "
+              "on one MI355X; see the sharding design notes).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import activation_sparse_decode_relu_amd as pi
+    from synth import config_by_name, make_layer, make_tokens
+
+    cfg = config_by_name(args.config)
+    B, mode = args.batch, args.mode
+    if B not in cfg.batches and not (cfg.name == "toy" and B <= 16):
+        print(f"note: batch {B} is not one of {cfg.name}'s configured batches {cfg.batches}", file=sys.stderr)
+    L = args.layers or cfg.n_layers
+    T = max(1, min(args.tokens, cfg.tokens // B))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- setup: every layer resident in HBM --------------------------------------------------
+    t_setup = time.time()
+    handles, xs, ys, idxs = [], [], [], []
+    host_sample = {}
+    sample_layers = sorted({0, L // 2})
+    ws = None
+    for l in range(L):
+        layer = make_layer(cfg, l, with_predictor=(mode == "predicted"))
+        h = pi.upload_layer(layer, dev, max_batch=B, workspace=ws)
+        ws = h.workspace
+        handles.append(h)
+        if l in sample_layers and not args.no_cpu:
+            host_sample[l] = layer
+        xs.append(torch.from_numpy(make_tokens(cfg, l, T * B)).to(dev))
+        ys.append(torch.empty((B, cfg.d_model), dtype=xs[-1].dtype, device=dev))
+        idxs.append(torch.empty(cfg.d_ffn, dtype=torch.int32, device=dev))
+        del layer
+        if l % 8 == 7 or l == L - 1:
+            print(f"[bench] {cfg.name}: {l + 1}/{L} layers resident ({time.time() - t_setup:.0f} s)", file=sys.stderr,
+                  flush=True)
+    counts = torch.zeros((T, L), dtype=torch.int32, device=dev)
+
+    def token_step(t: int) -> None:
+        for l in range(L):
+            handles[l].forward(xs[l][t * B:(t + 1) * B], ys[l], mode, idxs[l], counts[t, l:l + 1])
+
+    # ---- capture one graph per distinct token -------------------------------------------------
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(cap):
+        token_step(0)
+        cap.synchronize()
+        for t in range(T):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                token_step(t)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    print(f"[bench] captured {T} token graphs x {L} layers", file=sys.stderr, flush=True)
+
+    # ---- timed region --------------------------------------------------------------------------
+    for k in range(args.warmup):
+        graphs[k % T].replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for k in range(args.steps):
+        graphs[k % T].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    print(f"[bench] timed {args.steps} steps: {ms:.2f} ms", file=sys.stderr, flush=True)
+
+    cnt = counts.cpu().numpy().astype(np.int64)          # [T][L], deterministic per (token, layer)
+    bytes_per_token = np.array([sum(step_bytes(cfg, mode, B, int(cnt[t, l])) for l in range(L)) for t in range(T)])
+    total_bytes = sum(bytes_per_token[k % T] for k in range(args.steps))
+    sec = ms / 1e3
+    layers_per_s = L * args.steps / sec
+    gbps = total_bytes / sec / 1e9
+
+    # ---- per-kernel durations: HIP events around each kernel, eager, behind a queued backlog ---
+    phase_stats = {}
+    n_prof = min(args.profile_tokens, T)
+    for phase in PHASES_BY_MODE[mode]:
+        durs, nbytes = [], []
+        for t in range(n_prof):
+            starts = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
+            stops = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
+            for e in starts + stops:                        # create the underlying hipEvents
+                e.record()
+            torch.cuda.synchronize()
+            for k in range(4):                              # keep the GPU busy while the host enqueues
+                graphs[(t + k + 1) % T].replay()
+            for l in range(L):
+                handles[l].profile_next(phase, starts[l], stops[l])
+                handles[l].forward(xs[l][t * B:(t + 1) * B], ys[l], mode, idxs[l], counts[t, l:l + 1])
+            torch.cuda.synchronize()
+            for l in range(L):
+                durs.append(starts[l].elapsed_time(stops[l]) * 1e-3)
+                nbytes.append(phase_bytes(cfg, mode, phase, B, int(cnt[t, l])))
+        tot_s = sum(durs)
+        phase_stats[phase] = {"avg_us": 1e6 * tot_s / len(durs), "launches": len(durs),
+                              "alg_bytes_per_launch": sum(nbytes) / len(nbytes),
+                              "achieved_gbps": sum(nbytes) / tot_s / 1e9,
+                              "frac_of_peak": sum(nbytes) / tot_s / 1e9 / HBM_PEAK_GBPS}
+    dom = max(phase_stats, key=lambda p: phase_stats[p]["avg_us"])
+    ds = phase_stats[dom]
+    sum_kernels_us = sum(v["avg_us"] for v in phase_stats.values())
+
+    workload = f"{cfg.name}-{mode}-b{B}"
+    traffic = stored_traffic(dom, workload)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ds["achieved_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(ds["achieved_gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "avg_launch_us": round(ds["avg_us"], 3),
+                "alg_bytes_per_launch": round(ds["alg_bytes_per_launch"])}
+
+    cpu = None
+    if not args.no_cpu:
+        print(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, mode, B, host_sample, args.cpu_seconds)
+
+    mean_count = float(cnt.mean())
+    out = {
+        "metric": METRIC,
+        "value": round(layers_per_s, 1),
+        "unit": "layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.w_dtype if cfg.w_dtype != "q4g32" else "q4g32+f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.workload, "name": cfg.name, "mode": mode, "batch": B, "layers": L,
+                   "d_model": cfg.d_model, "d_ffn": cfg.d_ffn, "rank": cfg.rank, "gated": cfg.gated,
+                   "act_dtype": cfg.act_dtype, "accumulate": "f32", "distinct_tokens": T,
+                   "mean_active_neurons": round(mean_count, 1), "timing": "hipGraph per token, hipEvents"},
+        "effective_hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "ffn_tokens_per_s": round(layers_per_s * B / L, 1),
+        "alg_bytes_per_layer_step": round(float(bytes_per_token.mean()) / L),
+        "us_per_layer_step": round(1e6 * sec / (L * args.steps), 3),
+        "kernel_sum_us_per_layer_step": round(sum_kernels_us, 3),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in phase_stats.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+    for h in handles:
+        h.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

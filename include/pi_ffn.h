@@ -47,7 +47,8 @@
  *   enqueued.  PI_ERR_HIP reports a launch failure (or an earlier
  *   asynchronous fault surfacing at launch).  pi_last_error() returns a
  *   thread-local message for the last failing call on this thread.
- * - Pointers: every device pointer must be 16-byte aligned.
+ * - Pointers: weights, scales, biases, x, y and logits must be 16-byte
+ *   aligned; index lists and counts 4-byte aligned.
  */
 #ifndef PI_FFN_H
 #define PI_FFN_H
@@ -79,12 +80,10 @@ typedef enum pi_mask_mode {
 
 /* Kernels a profiling event pair can bracket (pi_ffn_profile_next). */
 typedef enum pi_phase {
-  PI_PHASE_PRED_HIDDEN = 0, /* h = ReLU(x P1^T)                                  */
-  PI_PHASE_PRED_MASK = 1,   /* z = h P2^T + b_p, threshold, ballot, compaction    */
-  PI_PHASE_DENSE_PRE = 2,   /* exact mode: dense pre-activation, mask, compaction */
-  PI_PHASE_GATHER = 3,      /* row-gather GEMV: a = ReLU(gate) (.) up            */
-  PI_PHASE_DOWN = 4,        /* active-row down projection + fixed-order reduce    */
-  PI_PHASE_COUNT = 5
+  PI_PHASE_PRED_HIDDEN = 0, /* h = ReLU(x P1^T)                                        */
+  PI_PHASE_GROUP = 1,       /* per neuron group: mask, row gather, ReLU(g)*u, partial y */
+  PI_PHASE_FINISH = 2,      /* fixed-order sum of the group partials; index list        */
+  PI_PHASE_COUNT = 3
 } pi_phase;
 
 typedef struct pi_ffn_desc {

@@ -256,3 +256,22 @@ def test_invalid_arguments_enqueue_nothing():
     with pytest.raises(pi.PiError):
         h.forward(x[:1], None, "dense")           # y is NULL
     h.close()
+
+
+@pytest.mark.parametrize("mode", ["predicted", "exact", "dense"])
+@pytest.mark.parametrize("B", [1, 4])
+def test_lattice_large_group_shape(mode, B):
+    """A layer wide enough for 128-neuron groups of 8 waves, with a ragged last group."""
+    d, n, r = 256, 16500, 64
+    announce(f"lattice large-group shape d={d} n={n} mode={mode} B={B}")
+    layer = make_lattice_layer(d, n, r, True, seed=21)
+    x = make_lattice_tokens(d, B, seed=22)
+    ref = oracle.forward(layer, x, mode)
+    h = _pi().upload_layer(layer, "cuda", max_batch=4)
+    idx, count, y = run_forward(h, x, mode)
+    assert count == ref["count"] and np.array_equal(idx, ref["idx"])
+    assert np.array_equal(y.view(np.uint8), ref["y"].view(np.uint8))
+    sel = ref["idx"][::3]
+    ym = run_masked(h, x, sel)
+    assert np.array_equal(ym.view(np.uint8), oracle.forward_masked(layer, x, sel)["y"].view(np.uint8))
+    h.close()
