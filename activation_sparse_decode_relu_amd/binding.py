@@ -165,8 +165,11 @@ class FFNLayer:
 
     def profile_next(self, phase, start_event, stop_event) -> None:
         p = PHASES[phase] if isinstance(phase, str) else int(phase)
-        s0 = None if start_event is None else int(start_event.cuda_event)
-        s1 = None if stop_event is None else int(stop_event.cuda_event)
+        def handle(ev):
+            if ev is None:
+                return None
+            return int(getattr(ev, "cuda_event", ev))    # a torch event or a raw hipEvent_t
+        s0, s1 = handle(start_event), handle(stop_event)
         check(LIB.pi_ffn_profile_next(self.handle, p, s0, s1))
 
 

@@ -49,7 +49,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Layout {
   size_t h, mask, idx, count, partial, total;
-  int group, waves, n_groups, n_words;
+  int group, waves, n_groups, n_words, max_partials;
 };
 
 // Neurons per group workgroup and waves per workgroup for a layer.  Small
@@ -78,7 +78,9 @@ Layout layout_for(const pi_ffn_desc& d) {
   L.mask = off;    off = align_up(off + sizeof(unsigned) * (size_t)L.n_words);
   L.idx = off;     off = align_up(off + sizeof(int) * n);
   L.count = off;   off = align_up(off + sizeof(int));
-  L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.n_groups * B * dm);
+  // partials: one [B][d] block per group workgroup
+  L.max_partials = L.n_groups;
+  L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.max_partials * B * dm);
   L.total = off;
   return L;
 }
@@ -148,6 +150,8 @@ struct pi_ffn {
 
 namespace {
 
+hipError_t record_event(void* ev, hipStream_t s) { return hipEventRecord(static_cast<hipEvent_t>(ev), s); }
+
 // Launch one phase, bracketed by the armed profiling events if any.
 template <typename F>
 pi_status run_phase(pi_ffn* h, int phase, hipStream_t s, const char* what, F&& launch) {
@@ -155,13 +159,15 @@ pi_status run_phase(pi_ffn* h, int phase, hipStream_t s, const char* what, F&& l
   void* ev1 = h->prof_stop[phase];
   if (ev0 != nullptr) {
     h->prof_start[phase] = h->prof_stop[phase] = nullptr;
-    if (hipEventRecord(static_cast<hipEvent_t>(ev0), s) != hipSuccess)
-      return fail(PI_ERR_HIP, "hipEventRecord before %s failed", what);
+    const hipError_t er = record_event(ev0, s);
+    if (er != hipSuccess) return fail(PI_ERR_HIP, "event record before %s failed: %s", what, hipGetErrorString(er));
   }
   const hipError_t e = launch();
   if (e != hipSuccess) return fail(PI_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
-  if (ev1 != nullptr && hipEventRecord(static_cast<hipEvent_t>(ev1), s) != hipSuccess)
-    return fail(PI_ERR_HIP, "hipEventRecord after %s failed", what);
+  if (ev1 != nullptr) {
+    const hipError_t er = record_event(ev1, s);
+    if (er != hipSuccess) return fail(PI_ERR_HIP, "event record after %s failed: %s", what, hipGetErrorString(er));
+  }
   return PI_OK;
 }
 
@@ -221,18 +227,21 @@ pi_status hidden_phase(pi_ffn* h, const void* x, int B, hipStream_t s) {
   });
 }
 
-pi_status group_phase(pi_ffn* h, int mode, const pik::GroupArgs& a, hipStream_t s) {
+// Runs the group kernel for this call; *partials receives the number of partials it wrote.
+pi_status group_phase(pi_ffn* h, int mode, const pik::GroupArgs& a, hipStream_t s, int* partials) {
+  const pi_ffn_desc& d = h->desc;
+  *partials = h->L.n_groups;
   return run_phase(h, PI_PHASE_GROUP, s, "ffn_group",
-                   [&] { return pik::launch_ffn_group(h->desc.w_dtype, h->desc.act_dtype, mode, a, s); });
+                   [&] { return pik::launch_ffn_group(d.w_dtype, d.act_dtype, mode, a, s); });
 }
 
-// reduce: sum the group partials into y; list: 0 = none, 1 = compact the mask words, 2 = 0..n-1
-pi_status finish_phase(pi_ffn* h, int B, void* y, bool reduce, int list, int* idx, int* count, hipStream_t s) {
+// reduce: sum the partials into y; list: 0 = none, 1 = compact the mask words, 2 = 0..n-1
+pi_status finish_phase(pi_ffn* h, int B, int partials, void* y, bool reduce, int list, int* idx, int* count,
+                       hipStream_t s) {
   const pi_ffn_desc& d = h->desc;
   return run_phase(h, PI_PHASE_FINISH, s, "finish", [&] {
-    return pik::launch_finish(d.act_dtype, h->partial(), h->L.n_groups, B, d.d_model, y,
-                              list == 1 ? h->mask() : nullptr, h->L.n_words, list == 2 ? d.d_ffn : 0, idx, count,
-                              reduce, list != 0, s);
+    return pik::launch_finish(d.act_dtype, h->partial(), partials, B, d.d_model, y, list == 1 ? h->mask() : nullptr,
+                              h->L.n_words, list == 2 ? d.d_ffn : 0, idx, count, reduce, list != 0, s);
   });
 }
 
@@ -274,7 +283,6 @@ pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights, 
   h->ws_bytes = workspace_bytes;
   h->L = L;
   h->thr = desc->rank > 0 ? (float)std::log((double)desc->tau / (1.0 - (double)desc->tau)) : 0.0f;
-
   // Clear the mask words once so a predict() before any forward() never reads garbage.
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pik::launch_fill_u32(h->mask(), L.n_words, 0u, s);
@@ -306,9 +314,10 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, 
   pik::GroupArgs a = group_args(h, x, batch);
   a.logits = logits_dbg;
   a.mask_only = 1;
+  int partials = 0;
   if ((st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
-  if ((st = group_phase(h, pik::MODE_PRED, a, s)) != PI_OK) return st;
-  if ((st = finish_phase(h, batch, nullptr, false, 1, idx, count, s)) != PI_OK) return st;
+  if ((st = group_phase(h, pik::MODE_PRED, a, s, &partials)) != PI_OK) return st;
+  if ((st = finish_phase(h, batch, partials, nullptr, false, 1, idx, count, s)) != PI_OK) return st;
   return ok();
 }
 
@@ -342,9 +351,10 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
     default:
       return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
   }
+  int partials = 0;
   if (mode == pik::MODE_PRED && (st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
-  if ((st = group_phase(h, mode, a, s)) != PI_OK) return st;
-  if ((st = finish_phase(h, batch, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
+  if ((st = group_phase(h, mode, a, s, &partials)) != PI_OK) return st;
+  if ((st = finish_phase(h, batch, partials, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
   return ok();
 }
 
@@ -358,8 +368,9 @@ pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const i
   pik::GroupArgs a = group_args(h, x, batch);
   a.list = idx;
   a.list_count = count;
-  if ((st = group_phase(h, pik::MODE_LIST, a, s)) != PI_OK) return st;
-  if ((st = finish_phase(h, batch, y, true, 0, nullptr, nullptr, s)) != PI_OK) return st;
+  int partials = 0;
+  if ((st = group_phase(h, pik::MODE_LIST, a, s, &partials)) != PI_OK) return st;
+  if ((st = finish_phase(h, batch, partials, y, true, 0, nullptr, nullptr, s)) != PI_OK) return st;
   return ok();
 }
 

@@ -25,6 +25,8 @@
 // No kernel communicates between workgroups inside a launch; every hand-off
 // goes through a kernel boundary.  Reductions use one fixed order, so results
 // are bit-reproducible run to run.
+#pragma once
+
 #include <type_traits>
 
 #include "device_common.h"
@@ -60,7 +62,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
 // count, by one workgroup.  Each thread owns a contiguous run of words; a scan
 // of the per-thread popcounts gives every thread its output offset, so the
 // list comes out in order.
-__device__ void block_compact(const unsigned* words, int n_words, int* idx, int* count) {
+__device__ inline void block_compact(const unsigned* words, int n_words, int* idx, int* count) {
   const int T = blockDim.x, tid = threadIdx.x;
   const int wpt = (n_words + T - 1) / T;
   const int w0 = min(tid * wpt, n_words), w1 = min(w0 + wpt, n_words);
@@ -79,7 +81,7 @@ __device__ void block_compact(const unsigned* words, int n_words, int* idx, int*
   if (tid == 0) *count = total;
 }
 
-__global__ void k_fill_u32(unsigned* p, int n, unsigned v) {
+__global__ inline void k_fill_u32(unsigned* p, int n, unsigned v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
 }
@@ -215,7 +217,10 @@ constexpr int kNWMax = 8;      // waves per group workgroup (4 or 8)
 constexpr int kGMax = 128;     // largest group
 
 // Selected neurons per gather batch: the batch's gate/up/down pieces are all in flight at once.
-template <int WT, int CPL> struct Batch { static constexpr int JB = ((WT == DT_Q4) ? 4 : 8) / CPL > 0 ? ((WT == DT_Q4) ? 4 : 8) / CPL : 1; };
+template <int WT, int CPL, int NB = 1> struct Batch {
+  static constexpr int kBase = ((WT == DT_Q4) ? 4 : 8) / CPL / (NB > 1 ? 2 : 1);
+  static constexpr int JB = kBase > 0 ? kBase : 1;
+};
 constexpr int kJBMax = 8;
 
 template <int WT, int AT, int NB, int MODE, int CPL, int NW>
@@ -230,27 +235,23 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
   const int g0 = grp * G;
   const XT* xb = static_cast<const XT*>(A.x);
 
-  __shared__ unsigned s_mask[kGMax / 32];
+  __shared__ unsigned s_wb[kNWMax];  // each wave's decision bits
   __shared__ int s_list[kGMax];
   __shared__ int s_m;
-  __shared__ float s_bias[kGMax];    // b of the group's neurons
-  __shared__ float s_bpre[kGMax];    // b_p (predictor) of the group's neurons
   __shared__ float s_g[(MODE == MODE_EXACT) ? kGMax * kMaxTokens : 1];
   __shared__ float s_part[kJBMax][2][NB][NW];
   __shared__ float s_a[kJBMax][NB];
 
-  // biases of the group's own neurons, fetched once up front
-  if (MODE != MODE_LIST && (int)threadIdx.x < G) {
-    const int i = g0 + threadIdx.x;
-    s_bias[threadIdx.x] = i < n ? A.b[i] : 0.f;
-    if (MODE == MODE_PRED) s_bpre[threadIdx.x] = i < n ? A.b_p[i] : 0.f;
-  }
-
   // ---- which neurons of the group are computed ------------------------------------------------
   if (MODE == MODE_PRED || MODE == MODE_EXACT) {
-    if (threadIdx.x < kGMax / 32) s_mask[threadIdx.x] = 0u;
-    __syncthreads();
-    const int rpw = G / NW;   // rows per wave, <= 32
+    const int rpw = G / NW;   // rows per wave: 4, 8, 16 or 32, so no wave's rows straddle a mask word
+    // Lane l holds the bias of the wave's row l (b_p, or b in exact mode); it is fetched ahead of
+    // the row loads and read back with readlane, so no global round trip precedes the row stream.
+    float row_bias = 0.f;
+    {
+      const int row = g0 + wave * rpw + lane;
+      if (lane < rpw && row < n) row_bias = (MODE == MODE_PRED) ? A.b_p[row] : A.b[row];
+    }
     constexpr int RB = (MODE == MODE_PRED) ? 8 : 4;
     bool dec = false;
 #pragma unroll 1
@@ -278,12 +279,14 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
           const f16* spre = A.gated ? A.s_gate : A.s_up;
           rows_dot<WT, AT, NB, RB, 4>(acc, static_cast<const char*>(wpre), row_bytes(WT, d), spre, d, rows, xb, t0, B);
         }
-        const float* bias = (MODE == MODE_PRED) ? s_bpre : s_bias;
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
+          // rb + j < rpw + RB <= 40: a valid lane even for the padding rows, whose value is unused
+          const float bias = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row_bias), rb + j));
 #pragma unroll
           for (int t = 0; t < NB; ++t) {
-            const float v = wave_sum(acc[j][t]) + (rows[j] >= 0 ? bias[wave * rpw + rb + j] : 0.f);
+            const float v = wave_sum(acc[j][t]) + bias;
             if (rows[j] >= 0 && t0 + t < B) {
               if (MODE == MODE_PRED && A.logits != nullptr && lane == 0) A.logits[(size_t)(t0 + t) * n + rows[j]] = v;
               if (MODE == MODE_EXACT && lane == 0) s_g[(wave * rpw + rb + j) * kMaxTokens + t0 + t] = v;
@@ -296,27 +299,30 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
       for (int j = 0; j < RB; ++j)
         if (lane == rb + j) dec = any[j];
     }
-    // lane j of the wave holds row (wave * rpw + j); place the wave's bits in the group's words
+    // lane j of the wave holds row (wave * rpw + j)
     const unsigned long long bits = __ballot(dec) & ((1ull << rpw) - 1ull);
-    if (lane == 0 && bits) {
-      const int bit0 = wave * rpw;
-      atomicOr(&s_mask[bit0 / 32], (unsigned)(bits << (bit0 % 32)));
-      if (bit0 % 32 + rpw > 32) atomicOr(&s_mask[bit0 / 32 + 1], (unsigned)(bits >> (32 - bit0 % 32)));
-    }
+    if (lane == 0) s_wb[wave] = (unsigned)bits;
     __syncthreads();
+    // word q of the group = the bits of waves q * (32 / rpw) ... (q + 1) * (32 / rpw) - 1
+    const int wpw = 32 / rpw;
+    auto group_word = [&](int q) {
+      unsigned w = 0u;
+      for (int k = 0; k < wpw; ++k) w |= s_wb[q * wpw + k] << (k * rpw);
+      return w;
+    };
     const int n_gw = G / 32;
     if ((int)threadIdx.x < n_gw && g0 / 32 + (int)threadIdx.x < (n + 31) / 32)
-      A.mask_words[g0 / 32 + threadIdx.x] = s_mask[threadIdx.x];
+      A.mask_words[g0 / 32 + threadIdx.x] = group_word(threadIdx.x);
     if ((int)threadIdx.x < G) {
       const int q = threadIdx.x / 32, bit = threadIdx.x % 32;
-      const unsigned word = s_mask[q];
+      const unsigned word = group_word(q);
       int pos = __popc(word & ((1u << bit) - 1u));
-      for (int qq = 0; qq < q; ++qq) pos += __popc(s_mask[qq]);
+      for (int qq = 0; qq < q; ++qq) pos += __popc(group_word(qq));
       if ((word >> bit) & 1u) s_list[pos] = threadIdx.x;
     }
     if (threadIdx.x == 0) {
       int m = 0;
-      for (int q = 0; q < n_gw; ++q) m += __popc(s_mask[q]);
+      for (int q = 0; q < n_gw; ++q) m += __popc(group_word(q));
       s_m = m;
     }
   } else if (MODE == MODE_DENSE) {
@@ -378,6 +384,17 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
         if (j < m) id = (MODE == MODE_LIST) ? s_list[j] : g0 + s_list[j];
         nid[jj] = id;
       }
+      // the activation threads fetch their neuron's bias along with the batch's rows
+      float bj = 0.f;
+      bool act_ok = false;
+      if ((int)threadIdx.x < kJB * NB) {
+        const int j = j0 + (int)threadIdx.x / NB;
+        if (j < m) {
+          const int id = (MODE == MODE_LIST) ? s_list[j] : g0 + s_list[j];
+          act_ok = id >= 0;
+          if (MODE != MODE_EXACT && act_ok) bj = A.b[id];
+        }
+      }
       // issue every load of the batch: gate, up and down pieces of this wave's slice
       u32x4 wg[kJB][CPL], wu[kJB][CPL], wd[kJB][CPL];
       float sg[kJB][CPL], su[kJB][CPL], sd[kJB][CPL];
@@ -431,7 +448,7 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
       if ((int)threadIdx.x < kJB * NB) {
         const int jj = threadIdx.x / NB, t = threadIdx.x % NB;
         float a = 0.f;
-        if (j0 + jj < m && nid[jj] >= 0 && t0 + t < B) {
+        if (act_ok && t0 + t < B) {
           float sg_ = 0.f, su_ = 0.f;
 #pragma unroll
           for (int w = 0; w < NW; ++w) {
@@ -442,7 +459,6 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
             const float g = s_g[s_list[j0 + jj] * kMaxTokens + t0 + t];
             a = A.gated ? fmaxf(g, 0.f) * su_ : fmaxf(g, 0.f);
           } else {
-            const float bj = (MODE == MODE_LIST) ? A.b[nid[jj]] : s_bias[s_list[j0 + jj]];
             a = A.gated ? fmaxf(sg_ + bj, 0.f) * su_ : fmaxf(su_ + bj, 0.f);
           }
         }
@@ -505,140 +521,53 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
     }
     return;
   }
-  // 256 threads = 16 column quads (64 columns) x 16 slices of the groups
-  __shared__ f32x4 s_red[16][16];
-  const int cq = threadIdx.x % 16, q = threadIdx.x / 16;
-  const int col = blockIdx.x * 64 + cq * 4;
+  // 256 threads = 8 column quads (32 columns: one 128-byte line of each partial row) x 32 slices
+  // of the groups.  Slice k sums groups k, k + 32, k + 64, ... in that order; the 32 slice sums
+  // are then added pairwise in a fixed tree, so the result is the same on every run.
+  constexpr int kQ = 8, kS = 32, kU = 12;
+  __shared__ f32x4 s_red[kS][kQ];
+  const int cq = threadIdx.x % kQ, sl = threadIdx.x / kQ;
+  const int col = blockIdx.x * (4 * kQ) + cq * 4;
   YT* yo = static_cast<YT*>(y);
   for (int t = 0; t < B; ++t) {
     f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     if (col < d) {
-      for (int g0 = q; g0 < NG; g0 += 16 * 8) {
-        f32x4 v[8];
+      for (int g0 = sl; g0 < NG; g0 += kS * kU) {
+        f32x4 v[kU];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int g = g0 + 16 * u;
+        for (int u = 0; u < kU; ++u) {
+          const int g = g0 + kS * u;
           v[u] = g < NG ? *reinterpret_cast<const f32x4*>(partial + ((size_t)g * B + t) * d + col)
                         : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sum += v[u];
+        for (int u = 0; u < kU; ++u) sum += v[u];
       }
     }
-    s_red[q][cq] = sum;
+    s_red[sl][cq] = sum;
     __syncthreads();
-    if (q == 0 && col < d) {
-      f32x4 tot = s_red[0][cq];
 #pragma unroll
-      for (int k = 1; k < 16; ++k) tot += s_red[k][cq];
+    for (int stride = kS / 2; stride > 0; stride /= 2) {
+      if (sl < stride) s_red[sl][cq] += s_red[sl + stride][cq];
+      __syncthreads();
+    }
+    if (sl == 0 && col < d) {
+      const f32x4 tot = s_red[0][cq];
 #pragma unroll
       for (int e = 0; e < 4; ++e) yo[(size_t)t * d + col + e] = from_f32<YT>(tot[e]);
     }
-    __syncthreads();
   }
 }
 
-// ---------------------------------------------------------------------------
-// Host-side launchers: runtime dtypes -> template instances.
-// ---------------------------------------------------------------------------
-namespace {
-constexpr int kBlock = 256;
-
+// Batch size B -> token block NB (1, or 4 with a loop over token blocks).
 template <typename F>
-hipError_t with_nb(int B, F&& f) {
+inline hipError_t with_nb(int B, F&& f) {
   if (B == 1) return f(std::integral_constant<int, 1>{});
   return f(std::integral_constant<int, 4>{});
 }
-}  // namespace
 
-int group_cpl(int wt, int d, int nw) {
-  const int epc = wt == DT_F32 ? 4 : (wt == DT_F16 ? 8 : 32);
-  const int nch = d / epc;
-  const int cpw = (nch + nw - 1) / nw;
-  return cpw <= 64 ? 1 : (cpw <= 128 ? 2 : (cpw <= 256 ? 4 : 0));
-}
-
-hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_u32, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p, n, v);
-  return hipGetLastError();
-}
-
-hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int d, int r, int B, float* h,
-                              hipStream_t s) {
-  const dim3 grid((r + 3) / 4), block(kBlock);
-  return with_nb(B, [&](auto nbc) -> hipError_t {
-    constexpr int NB = decltype(nbc)::value;
-    constexpr int U = 8;
-    if (pt == DT_F16 && at == DT_F16)
-      hipLaunchKernelGGL((k_pred_hidden<DT_F16, DT_F16, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
-    else if (pt == DT_F16 && at == DT_F32)
-      hipLaunchKernelGGL((k_pred_hidden<DT_F16, DT_F32, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
-    else if (pt == DT_F32 && at == DT_F16)
-      hipLaunchKernelGGL((k_pred_hidden<DT_F32, DT_F16, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
-    else if (pt == DT_F32 && at == DT_F32)
-      hipLaunchKernelGGL((k_pred_hidden<DT_F32, DT_F32, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
-    else
-      return hipErrorInvalidValue;
-    return hipGetLastError();
-  });
-}
-
-hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s) {
-  const int ng = (a.n + a.G - 1) / a.G;
-  if (a.G % 32 != 0 || a.G > kGMax || (a.nw != 4 && a.nw != 8) || a.G / a.nw > 32) return hipErrorInvalidValue;
-  const dim3 grid(ng), block(a.nw * WAVE);
-  const int cpl = group_cpl(wt, a.d, a.nw);
-  if (cpl == 0) return hipErrorInvalidValue;
-  return with_nb(a.B, [&](auto nbc) -> hipError_t {
-    constexpr int NB = decltype(nbc)::value;
-#define PIK_GRP(W, AC, M, C, NWV) hipLaunchKernelGGL((k_ffn_group<W, AC, NB, M, C, NWV>), grid, block, 0, s, a)
-#define PIK_GRP_NW(W, AC, M, C)                 \
-  do {                                          \
-    if (a.nw == 4) PIK_GRP(W, AC, M, C, 4);     \
-    else PIK_GRP(W, AC, M, C, 8);               \
-  } while (0)
-#define PIK_GRP_C(W, AC, M)                      \
-  do {                                           \
-    if (cpl == 1) PIK_GRP_NW(W, AC, M, 1);       \
-    else if (cpl == 2) PIK_GRP_NW(W, AC, M, 2);  \
-    else PIK_GRP_NW(W, AC, M, 4);                \
-  } while (0)
-#define PIK_GRP_M(W, AC)                                       \
-  do {                                                         \
-    if (mode == MODE_PRED) PIK_GRP_C(W, AC, MODE_PRED);        \
-    else if (mode == MODE_EXACT) PIK_GRP_C(W, AC, MODE_EXACT); \
-    else if (mode == MODE_DENSE) PIK_GRP_C(W, AC, MODE_DENSE); \
-    else PIK_GRP_C(W, AC, MODE_LIST);                          \
-  } while (0)
-    if (wt == DT_F16 && at == DT_F16) PIK_GRP_M(DT_F16, DT_F16);
-    else if (wt == DT_F16 && at == DT_F32) PIK_GRP_M(DT_F16, DT_F32);
-    else if (wt == DT_F32 && at == DT_F32) PIK_GRP_M(DT_F32, DT_F32);
-    else if (wt == DT_F32 && at == DT_F16) PIK_GRP_M(DT_F32, DT_F16);
-    else if (wt == DT_Q4 && at == DT_F16) PIK_GRP_M(DT_Q4, DT_F16);
-    else if (wt == DT_Q4 && at == DT_F32) PIK_GRP_M(DT_Q4, DT_F32);
-    else return hipErrorInvalidValue;
-#undef PIK_GRP_M
-#undef PIK_GRP_C
-#undef PIK_GRP_NW
-#undef PIK_GRP
-    return hipGetLastError();
-  });
-}
-
-hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
-                         const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,
-                         bool reduce, bool index_list, hipStream_t s) {
-  const int ncol = reduce ? (d + 63) / 64 : 0;
-  const int grid = ncol + (index_list ? 1 : 0);
-  if (grid == 0) return hipSuccess;
-  if (ot == DT_F16)
-    hipLaunchKernelGGL((k_finish<DT_F16>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
-                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
-  else
-    hipLaunchKernelGGL((k_finish<DT_F32>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
-                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
-  return hipGetLastError();
-}
+// Per-weight-format launchers, each compiled in its own translation unit.
+hipError_t launch_ffn_group_f16(int at, int mode, const GroupArgs& a, int cpl, hipStream_t s);
+hipError_t launch_ffn_group_other(int wt, int at, int mode, const GroupArgs& a, int cpl, hipStream_t s);
 
 }  // namespace pik

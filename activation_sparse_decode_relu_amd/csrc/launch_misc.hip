@@ -1,0 +1,67 @@
+// Host-side launchers: runtime dtypes -> template instances (small kernels here; the large
+// group kernels in their own translation units).
+#include "kernels_impl.h"
+
+namespace pik {
+
+namespace {
+constexpr int kBlock = 256;
+}  // namespace
+
+int group_cpl(int wt, int d, int nw) {
+  const int epc = wt == DT_F32 ? 4 : (wt == DT_F16 ? 8 : 32);
+  const int nch = d / epc;
+  const int cpw = (nch + nw - 1) / nw;
+  return cpw <= 64 ? 1 : (cpw <= 128 ? 2 : (cpw <= 256 ? 4 : 0));
+}
+
+hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u32, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int d, int r, int B, float* h,
+                              hipStream_t s) {
+  const dim3 grid((r + 3) / 4), block(kBlock);
+  return with_nb(B, [&](auto nbc) -> hipError_t {
+    constexpr int NB = decltype(nbc)::value;
+    constexpr int U = 8;
+    if (pt == DT_F16 && at == DT_F16)
+      hipLaunchKernelGGL((k_pred_hidden<DT_F16, DT_F16, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
+    else if (pt == DT_F16 && at == DT_F32)
+      hipLaunchKernelGGL((k_pred_hidden<DT_F16, DT_F32, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
+    else if (pt == DT_F32 && at == DT_F16)
+      hipLaunchKernelGGL((k_pred_hidden<DT_F32, DT_F16, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
+    else if (pt == DT_F32 && at == DT_F32)
+      hipLaunchKernelGGL((k_pred_hidden<DT_F32, DT_F32, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s) {
+  if (a.G % 32 != 0 || a.G > kGMax || (a.nw != 4 && a.nw != 8) || a.G / a.nw > 32) return hipErrorInvalidValue;
+  const int cpl = group_cpl(wt, a.d, a.nw);
+  if (cpl == 0) return hipErrorInvalidValue;
+  if (wt == DT_F16) return launch_ffn_group_f16(at, mode, a, cpl, s);
+  return launch_ffn_group_other(wt, at, mode, a, cpl, s);
+}
+
+hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
+                         const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,
+                         bool reduce, bool index_list, hipStream_t s) {
+  const int ncol = reduce ? (d + 31) / 32 : 0;   // 32 columns per workgroup
+  const int grid = ncol + (index_list ? 1 : 0);
+  if (grid == 0) return hipSuccess;
+  if (ot == DT_F16)
+    hipLaunchKernelGGL((k_finish<DT_F16>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
+                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
+  else
+    hipLaunchKernelGGL((k_finish<DT_F32>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
+                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
+  return hipGetLastError();
+}
+
+}  // namespace pik

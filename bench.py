@@ -112,6 +112,96 @@ def stored_traffic(kernel_phase: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+class HipEvent:
+    """A raw timing hipEvent_t.
+
+    Created with hipEventDisableSystemFence: a timing-only event then skips the system-scope
+    cache writeback and invalidate that a default event performs on record, which would
+    otherwise add microseconds to every bracketed kernel.
+    """
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so")
+            HipEvent._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            HipEvent._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                          ctypes.c_void_p]
+            HipEvent._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._ev = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._ev), HipEvent.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.cuda_event = self._ev.value
+
+    def elapsed_ms(self, stop: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self._ev, stop._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self._ev:
+            HipEvent._hip.hipEventDestroy(self._ev)
+
+
+def copy_calibration(mb: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = mb << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: 3 copies of {mb} MiB", file=sys.stderr, flush=True)
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, steps: int) -> dict:
+    """Per-launch HBM bytes of each kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files.
+
+    Each counter is scaled by what it reads for the plain copy of copy_mib MiB
+    (expected: copy_mib MiB fetched and written).
+    """
+    import csv
+    from collections import defaultdict
+
+    def load(path, counter):
+        per = defaultdict(list)
+        for row in csv.DictReader(open(path)):
+            if row.get("Counter_Name") != counter:
+                continue
+            per[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+        return per
+
+    fetch = load(fetch_csv, "FETCH_SIZE")
+    write = load(write_csv, "WRITE_SIZE")
+    copy_names = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    expect_kib = copy_mib * 1024.0
+    big_f = [v for k in copy_names for v in fetch[k] if v > 0.5 * expect_kib]
+    big_w = [v for k in copy_names for v in write.get(k, []) if v > 0.5 * expect_kib]
+    f_scale = expect_kib / (sum(big_f) / len(big_f)) if big_f else None
+    w_scale = expect_kib / (sum(big_w) / len(big_w)) if big_w else None
+    out = {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    phase_of = {"k_pred_hidden": "pred_hidden", "k_ffn_group": "group", "k_finish": "finish"}
+    for name, vals in fetch.items():
+        phase = next((p for k, p in phase_of.items() if k in name), None)
+        if phase is None or f_scale is None:
+            continue
+        wv = write.get(name, [])
+        f_b = 1024.0 * f_scale * sum(vals) / len(vals)
+        w_b = 1024.0 * w_scale * sum(wv) / len(wv) if wv and w_scale else None
+        out["kernels"][f"{workload}/{phase}"] = {
+            "kernel": name, "dispatches": len(vals), "fetch_bytes_per_launch": round(f_b),
+            "write_bytes_per_launch": None if w_b is None else round(w_b),
+            "bytes_per_launch": round(f_b + (w_b or 0.0)), "source_hash": source_hash()}
+    return out
+
+
 def cpu_baseline(cfg, mode: str, B: int, host_layers: dict, budget_s: float):
     """The CPU oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -124,13 +214,14 @@ def cpu_baseline(cfg, mode: str, B: int, host_layers: dict, budget_s: float):
         blas_threads = len(os.sched_getaffinity(0))
     done, elapsed = 0, 0.0
     per_layer = budget_s / max(1, len(host_layers))
+    ntok = min(cfg.tokens // B, 256)
     for l, layer in host_layers.items():
         # decode the stored weights once per layer, outside the timed region
         weights = (oracle.dense_weights(layer.w_gate, layer.s_gate) if layer.gated else None,
                    oracle.dense_weights(layer.w_up, layer.s_up), oracle.dense_weights(layer.w_down_t, layer.s_down))
-        x = make_tokens(cfg, l, 16 * B)
+        x = make_tokens(cfg, l, ntok * B)
         spent = 0.0
-        for t in range(16):
+        for t in range(ntok):
             t0 = time.perf_counter()
             oracle.forward(layer, x[t * B:(t + 1) * B], mode, weights=weights)
             spent += time.perf_counter() - t0
@@ -158,7 +249,28 @@ def main() -> int:
     ap.add_argument("--profile-tokens", type=int, default=4, help="tokens of the per-kernel event pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter files and exit")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        from synth import config_by_name
+        cfg = config_by_name(args.config)
+        res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_calib or 256,
+                            f"{cfg.name}-{args.mode}-b{args.batch}", args.steps)
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        try:
+            data = json.load(open(path))
+        except (OSError, ValueError):
+            data = {}
+        data.update(res["kernels"])
+        data.setdefault("_calibration", {})[f"{cfg.name}-{args.mode}-b{args.batch}"] = {
+            k: res[k] for k in ("copy_mib", "fetch_scale", "write_scale")}
+        json.dump(data, open(path, "w"), indent=1, sort_keys=True)
+        print(json.dumps(res, indent=1))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the sparse FFN path here runs "
@@ -179,6 +291,8 @@ def main() -> int:
     T = max(1, min(args.tokens, cfg.tokens // B))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
 
     # ---- setup: every layer resident in HBM --------------------------------------------------
     t_setup = time.time()
@@ -241,28 +355,29 @@ def main() -> int:
     layers_per_s = L * args.steps / sec
     gbps = total_bytes / sec / 1e9
 
-    # ---- per-kernel durations: HIP events around each kernel, eager, behind a queued backlog ---
+    # ---- per-kernel durations: HIP events around each kernel --------------------------------
+    # HIP records events under stream capture as dependencies, not timed nodes, so the
+    # instrumented pass is eager: a backlog of queued graph replays keeps the GPU busy while the
+    # host enqueues one token's L layers, each with an event pair around the phase's kernel.
     phase_stats = {}
     n_prof = min(args.profile_tokens, T)
     for phase in PHASES_BY_MODE[mode]:
         durs, nbytes = [], []
         for t in range(n_prof):
-            starts = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
-            stops = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
-            for e in starts + stops:                        # create the underlying hipEvents
-                e.record()
-            torch.cuda.synchronize()
-            for k in range(4):                              # keep the GPU busy while the host enqueues
+            starts = [HipEvent() for _ in range(L)]
+            stops = [HipEvent() for _ in range(L)]
+            for k in range(16):
                 graphs[(t + k + 1) % T].replay()
             for l in range(L):
                 handles[l].profile_next(phase, starts[l], stops[l])
                 handles[l].forward(xs[l][t * B:(t + 1) * B], ys[l], mode, idxs[l], counts[t, l:l + 1])
             torch.cuda.synchronize()
             for l in range(L):
-                durs.append(starts[l].elapsed_time(stops[l]) * 1e-3)
+                durs.append(starts[l].elapsed_ms(stops[l]) * 1e-3)
                 nbytes.append(phase_bytes(cfg, mode, phase, B, int(cnt[t, l])))
         tot_s = sum(durs)
-        phase_stats[phase] = {"avg_us": 1e6 * tot_s / len(durs), "launches": len(durs),
+        phase_stats[phase] = {"avg_us": 1e6 * tot_s / len(durs), "min_us": 1e6 * min(durs),
+                              "launches": len(durs),
                               "alg_bytes_per_launch": sum(nbytes) / len(nbytes),
                               "achieved_gbps": sum(nbytes) / tot_s / 1e9,
                               "frac_of_peak": sum(nbytes) / tot_s / 1e9 / HBM_PEAK_GBPS}

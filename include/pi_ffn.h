@@ -167,7 +167,10 @@ pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const i
  * Profiling: arm a one-shot event pair.  The next launch of `phase`'s kernel
  * by this handle is bracketed by hipEventRecord(start_event) and
  * hipEventRecord(stop_event) on the launch stream; then the pair disarms.
- * Events are hipEvent_t passed as void*.  Passing NULL events disarms.
+ * The elapsed time covers the launch from dispatch to completion.  Meant for
+ * eager calls: under stream capture HIP treats event records as capture
+ * dependencies, not timed nodes.  Events are hipEvent_t passed as void*.
+ * NULL events disarm.
  */
 pi_status pi_ffn_profile_next(pi_ffn* h, int32_t phase, void* start_event, void* stop_event);
 
