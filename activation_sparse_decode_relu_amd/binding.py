@@ -20,11 +20,12 @@ LIB_PATH = os.environ.get("PI_FFN_LIB", os.path.join(PKG_DIR, "libpi_ffn.so"))
 PI_OK, PI_ERR_INVALID, PI_ERR_WORKSPACE, PI_ERR_HIP, PI_ERR_UNSUPPORTED = range(5)
 PI_F32, PI_F16, PI_Q4G32 = range(3)
 PI_MASK_PREDICTED, PI_MASK_EXACT_RELU, PI_MASK_DENSE = range(3)
-PI_PHASE_PRED_HIDDEN, PI_PHASE_GROUP, PI_PHASE_FINISH, PI_PHASE_COUNT = range(4)
+PI_PHASE_PRED_HIDDEN, PI_PHASE_GROUP, PI_PHASE_DOWN, PI_PHASE_FINISH, PI_PHASE_COUNT = range(5)
 
 DTYPES = {"f32": PI_F32, "f16": PI_F16, "q4g32": PI_Q4G32}
 MODES = {"predicted": PI_MASK_PREDICTED, "exact": PI_MASK_EXACT_RELU, "dense": PI_MASK_DENSE}
-PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "group": PI_PHASE_GROUP, "finish": PI_PHASE_FINISH}
+PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "group": PI_PHASE_GROUP, "down": PI_PHASE_DOWN,
+          "finish": PI_PHASE_FINISH}
 STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_ERR_HIP", 4: "PI_ERR_UNSUPPORTED"}
 
 EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",

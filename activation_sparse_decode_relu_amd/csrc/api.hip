@@ -10,6 +10,7 @@
 //   forward_masked     ffn_group(caller's list) -> finish
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -48,7 +49,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t h, mask, idx, count, partial, total;
+  size_t h, mask, idx, count, abuf, partial, total;
   int group, waves, n_groups, n_words, max_partials;
 };
 
@@ -78,8 +79,11 @@ Layout layout_for(const pi_ffn_desc& d) {
   L.mask = off;    off = align_up(off + sizeof(unsigned) * (size_t)L.n_words);
   L.idx = off;     off = align_up(off + sizeof(int) * n);
   L.count = off;   off = align_up(off + sizeof(int));
-  // partials: one [B][d] block per group workgroup
+  // activations of the batched matrix-core path: a[neuron][16] fp32
+  L.abuf = off;    off = align_up(off + (d.max_batch > 1 ? sizeof(float) * n * pik::kMaxTokens : 0));
+  // partials: one [B][d] block per group workgroup, or per down chunk on the batched path
   L.max_partials = L.n_groups;
+  if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
   L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.max_partials * B * dm);
   L.total = off;
   return L;
@@ -146,6 +150,7 @@ struct pi_ffn {
   int* idx() const { return reinterpret_cast<int*>(ws + L.idx); }
   int* count() const { return reinterpret_cast<int*>(ws + L.count); }
   float* partial() const { return reinterpret_cast<float*>(ws + L.partial); }
+  float* abuf() const { return reinterpret_cast<float*>(ws + L.abuf); }
 };
 
 namespace {
@@ -227,9 +232,19 @@ pi_status hidden_phase(pi_ffn* h, const void* x, int B, hipStream_t s) {
   });
 }
 
-// Runs the group kernel for this call; *partials receives the number of partials it wrote.
+// Runs the group kernel (and, on the batched matrix-core path, the down kernel) for this
+// call; *partials receives the number of partials of y written.
 pi_status group_phase(pi_ffn* h, int mode, const pik::GroupArgs& a, hipStream_t s, int* partials) {
   const pi_ffn_desc& d = h->desc;
+  if (pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, a.B, d.d_model, d.rank)) {
+    pi_status st = run_phase(h, PI_PHASE_GROUP, s, "ffn_bgroup",
+                             [&] { return pik::launch_ffn_bgroup(mode, a, h->abuf(), s); });
+    if (st != PI_OK || a.mask_only) return st;
+    const int chunks = pik::batch_down_chunks(d.d_model);
+    *partials = chunks;
+    return run_phase(h, PI_PHASE_DOWN, s, "ffn_bdown",
+                     [&] { return pik::launch_ffn_bdown(mode, a, h->abuf(), chunks, s); });
+  }
   *partials = h->L.n_groups;
   return run_phase(h, PI_PHASE_GROUP, s, "ffn_group",
                    [&] { return pik::launch_ffn_group(d.w_dtype, d.act_dtype, mode, a, s); });
@@ -342,6 +357,7 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
       break;
     case PI_MASK_EXACT_RELU:
       mode = pik::MODE_EXACT;
+      a.thr = 0.0f;   // the ReLU support: g > 0, whatever the predictor's tau
       list = 1;
       break;
     case PI_MASK_DENSE:

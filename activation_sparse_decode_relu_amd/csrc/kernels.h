@@ -42,6 +42,15 @@ hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int
 
 hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s);
 
+// The batched matrix-core path (2..16 tokens, fp16 weights, activations and predictor):
+// k_ffn_bgroup writes the mask words and a[neuron][16] (fp32) into abuf; k_ffn_bdown writes
+// batch_down_chunks(d) partials of y.
+bool batch_supported(int wt, int at, int pt, int B, int d, int r);
+int batch_groups(int n);
+int batch_down_chunks(int d);
+hipError_t launch_ffn_bgroup(int mode, const GroupArgs& a, float* abuf, hipStream_t s);
+hipError_t launch_ffn_bdown(int mode, const GroupArgs& a, const float* abuf, int chunks, hipStream_t s);
+
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
                          const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,
                          bool reduce, bool index_list, hipStream_t s);

@@ -1,0 +1,414 @@
+// Batched decode steps (2 to 16 tokens; fp16 weights, activations and predictor) on the
+// CDNA4 matrix cores.
+//
+// With a batch, every gathered row serves B tokens, so the row-gather products become
+// skinny GEMMs.  Tokens are padded to 16, the M dimension of the 16x16 MFMA tiles.  Each
+// of these products must, by construction, contract over the dimension that is contiguous
+// in memory:
+//
+//   k_ffn_bgroup  one workgroup per group of 64 neurons, 4 waves, each wave taking a
+//                 quarter of the contraction:
+//                   mask  predicted: Z = H P2^T (fp32 MFMA: h stays fp32, the fp16
+//                         predictor rows are widened exactly); exact: the dense
+//                         pre-activation X W^T (fp16 MFMA, fp32 accumulation).  The union
+//                         over the batch's tokens gives the group's mask words.
+//                   act   gate and up products of the active neurons (fp16 MFMA, exact
+//                         fp16 products, fp32 accumulation), a fixed-order sum of the four
+//                         waves' partial tiles, a = ReLU(g + b) * u (or ReLU(u + b)),
+//                         written to a[neuron][16] in fp32.
+//   k_ffn_bdown   y partials over (neuron chunk, 512-column slice): the contraction runs
+//                 over neurons, which are strided in W_down^T, so it uses the fp32 MFMA
+//                 whose lanes each supply a single element: lane l takes neuron (l / 16) of
+//                 a 4-neuron step and 8 consecutive columns of that neuron's row, one
+//                 column per output tile.  a stays fp32; the fp16 weights widen exactly.
+//
+// The pages describe the single-token step (PowerInfer paper explainer, section
+// "ニューロン活性化のべき乗則分布" for the FFN and "活性化予測器" for the predictor); the
+// batch union is the reading that a row loaded once serves every token that fires it.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pik {
+
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBG = 64;         // neurons per batched group workgroup
+constexpr int kBNW = 4;         // waves per batched group workgroup
+constexpr int kBT = kBG / 16;   // 16-neuron tiles per group
+constexpr int kDW = 4;          // waves per down workgroup
+constexpr int kDCols = 128;     // output columns per down wave: 8 MFMA tiles of 16
+constexpr int kDSeg = 2048;     // neurons a down workgroup compacts into LDS at a time
+constexpr int kDU = 8;          // 4-neuron steps per down iteration
+
+// D[16][16] += A[16][4] B[4][16] (fp32): lane l gives A[l%16][l/16] and B[l/16][l%16] and
+// holds D[4(l/16)+v][l%16] in element v.
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// D[16][16] += A[16][32] B[32][16] (fp16 in, fp32 accumulate): lane l gives A[l%16][8(l/16)+e]
+// and B[8(l/16)+e][l%16] for e = 0..7; D as above.
+__device__ __forceinline__ f32x4 mma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+__device__ __forceinline__ float half_at(u32x4 w, int e) { return (float)__builtin_bit_cast(f16x8, w)[e]; }
+
+// Partial tiles over this wave's share [k_begin, k_end) of a contraction of length K:
+// acc[m][t] += X[tok][k] * W_m[row[t]][k] for the nt tiles in use; rows < 0, tokens >= B and
+// k >= k_end contribute zeros.  MFMA k-steps of 32, double-buffered: the loads of the next
+// step are issued before the products of the current one.
+template <int NM>
+struct F16Step {
+  u32x4 xa, wv[NM][kBT];
+};
+
+template <int NM>
+__device__ __forceinline__ void f16_step_load(F16Step<NM>& b, const f16* const (&w)[NM], const int (&row)[kBT], int nt,
+                                              const f16* xr, bool xok, int K, int k0, int k_end) {
+  const int kk = k0 + 8 * ((threadIdx.x & (WAVE - 1)) >> 4);
+  const bool ok = k0 < k_end;
+  b.xa = (xok && ok) ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < kBT; ++t)
+      b.wv[m][t] = (ok && t < nt && row[t] >= 0)
+                       ? ld_stream(reinterpret_cast<const u32x4*>(w[m] + (size_t)row[t] * K + kk))
+                       : u32x4{0, 0, 0, 0};
+}
+
+template <int NM>
+__device__ __forceinline__ void f16_step_mma(f32x4 (&acc)[NM][kBT], const F16Step<NM>& b, int nt) {
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < kBT; ++t)
+      if (t < nt) acc[m][t] = mma_f16(b.xa, b.wv[m][t], acc[m][t]);
+}
+
+template <int NM>
+__device__ __forceinline__ void tiles_mma_f16(f32x4 (&acc)[NM][kBT], const f16* const (&w)[NM], const int (&row)[kBT],
+                                              int nt, const f16* __restrict__ x, int B, int K, int k_begin,
+                                              int k_end) {
+  const int li = threadIdx.x & 15;
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < kBT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f16* xr = x + (size_t)li * K;
+  const bool xok = li < B;
+  F16Step<NM> b0, b1;
+  f16_step_load(b0, w, row, nt, xr, xok, K, k_begin, k_end);
+  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
+    f16_step_load(b1, w, row, nt, xr, xok, K, k0 + 32, k_end);
+    f16_step_mma(acc, b0, nt);
+    if (k0 + 64 < k_end) f16_step_load(b0, w, row, nt, xr, xok, K, k0 + 64, k_end);
+    if (k0 + 32 < k_end) f16_step_mma(acc, b1, nt);
+  }
+}
+
+// Fixed-order sum over the waves of tile t's lane l partials, after each wave stored its own.
+__device__ __forceinline__ f32x4 wave_tiles_sum(const f32x4 (*red)[2][kBT][WAVE], int m, int t, int l) {
+  f32x4 s = red[0][m][t][l];
+#pragma unroll
+  for (int w = 1; w < kBNW; ++w) s += red[w][m][t][l];
+  return s;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, float* __restrict__ abuf) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, li = lane & 15, lk = lane >> 4;
+  const int B = A.B, d = A.d, n = A.n;
+  const int g0 = blockIdx.x * kBG;
+  const f16* xb = static_cast<const f16*>(A.x);
+
+  __shared__ f32x4 s_red[kBNW][2][kBT][WAVE];   // each wave's partial tiles
+  __shared__ float s_pre[(MODE == MODE_EXACT) ? kBG * kMaxTokens : 1];
+  __shared__ unsigned s_tbits[kBT];
+  __shared__ int s_list[kBG];
+  __shared__ int s_m;
+
+  // ---- which neurons of the group are computed ------------------------------------------------
+  if (MODE == MODE_PRED || MODE == MODE_EXACT) {
+    // this thread's tile (= its wave) and neuron, after the cross-wave sum
+    const int t = wave, nrn = g0 + 16 * t + li;
+    f32x4 z;
+    float bias = 0.f;
+    if (MODE == MODE_PRED) {
+      if (nrn < n) bias = A.b_p[nrn];
+      const int r = A.r, kw = r / kBNW, kb = wave * kw;
+      const f16* p2 = static_cast<const f16*>(A.p2);
+      const float* hr = A.h + (size_t)li * r;
+      f32x4 acc[kBT];
+#pragma unroll
+      for (int q = 0; q < kBT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      struct P2Step {
+        u32x4 pw[kBT];
+        f32x4 hv[2];
+      };
+      auto load = [&](P2Step& st, int k0) {
+        const int kk = k0 + 8 * lk;
+        const bool ok = k0 < kb + kw;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          st.hv[q] = (ok && li < B) ? *reinterpret_cast<const f32x4*>(hr + kk + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < kBT; ++q) {
+          const int row = g0 + 16 * q + li;
+          st.pw[q] = (ok && row < n) ? ld_stream(reinterpret_cast<const u32x4*>(p2 + (size_t)row * r + kk))
+                                     : u32x4{0, 0, 0, 0};
+        }
+      };
+      auto mma = [&](const P2Step& st) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int q = 0; q < kBT; ++q) acc[q] = mma_f32(st.hv[e / 4][e % 4], half_at(st.pw[q], e), acc[q]);
+      };
+      P2Step st0, st1;
+      load(st0, kb);
+      for (int k0 = kb; k0 < kb + kw; k0 += 64) {
+        load(st1, k0 + 32);
+        mma(st0);
+        if (k0 + 64 < kb + kw) load(st0, k0 + 64);
+        if (k0 + 32 < kb + kw) mma(st1);
+      }
+#pragma unroll
+      for (int q = 0; q < kBT; ++q) s_red[wave][0][q][lane] = acc[q];
+      __syncthreads();
+      z = wave_tiles_sum(s_red, 0, t, lane);
+    } else {
+      if (nrn < n) bias = A.b[nrn];
+      int row[kBT];
+#pragma unroll
+      for (int q = 0; q < kBT; ++q) row[q] = (g0 + 16 * q + li < n) ? g0 + 16 * q + li : -1;
+      const f16* const w[1] = {static_cast<const f16*>(A.gated ? A.w_gate : A.w_up)};
+      f32x4 acc[1][kBT];
+      const int kw = d / kBNW;
+      tiles_mma_f16<1>(acc, w, row, kBT, xb, B, d, wave * kw, (wave + 1) * kw);
+#pragma unroll
+      for (int q = 0; q < kBT; ++q) s_red[wave][0][q][lane] = acc[0][q];
+      __syncthreads();
+      z = wave_tiles_sum(s_red, 0, t, lane);
+    }
+    bool dec = false;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 4 * lk + v;
+      const float val = z[v] + bias;
+      if (MODE == MODE_EXACT) s_pre[(16 * t + li) * kMaxTokens + tok] = val;
+      if (nrn < n && tok < B) {
+        if (MODE == MODE_PRED && A.logits != nullptr) A.logits[(size_t)tok * n + nrn] = val;
+        dec = dec || (val > A.thr);
+      }
+    }
+    // neuron li of tile t fires if any of its four lanes (token quarters) saw it fire
+    const unsigned long long b = __ballot(dec);
+    if (lane == 0) s_tbits[t] = (unsigned)((b | (b >> 16) | (b >> 32) | (b >> 48)) & 0xFFFFull);
+    __syncthreads();
+    const unsigned long long gmask = (unsigned long long)s_tbits[0] | ((unsigned long long)s_tbits[1] << 16) |
+                                     ((unsigned long long)s_tbits[2] << 32) | ((unsigned long long)s_tbits[3] << 48);
+    const int n_words = (n + 31) / 32;
+    if ((int)threadIdx.x < kBG / 32 && g0 / 32 + (int)threadIdx.x < n_words)
+      A.mask_words[g0 / 32 + threadIdx.x] = (unsigned)(gmask >> (32 * threadIdx.x));
+    if ((int)threadIdx.x < kBG && ((gmask >> threadIdx.x) & 1ull))
+      s_list[__popcll(gmask & ((1ull << threadIdx.x) - 1ull))] = threadIdx.x;
+    if (threadIdx.x == 0) s_m = __popcll(gmask);
+  } else if (MODE == MODE_DENSE) {
+    if ((int)threadIdx.x < kBG) s_list[threadIdx.x] = threadIdx.x;
+    if (threadIdx.x == 0) s_m = max(0, min(kBG, n - g0));
+  } else {  // MODE_LIST: an even slice of the caller's list per workgroup
+    const int cnt = min(max(*A.list_count, 0), n);
+    const int per = (cnt + (int)gridDim.x - 1) / (int)gridDim.x;   // <= kBG since gridDim.x = ceil(n / kBG)
+    const int e0 = blockIdx.x * per;
+    const int m = max(0, min(per, cnt - e0));
+    if ((int)threadIdx.x < m) {
+      const int id = A.list[e0 + threadIdx.x];
+      s_list[threadIdx.x] = ((unsigned)id < (unsigned)n) ? id : -1;
+    }
+    if (threadIdx.x == 0) s_m = m;
+  }
+  __syncthreads();
+  if (A.mask_only) return;
+  const int m = s_m;
+  if (m == 0) return;
+  const int nt = (m + 15) / 16;
+
+  // ---- gate / up products of the active neurons, the activation, a[neuron][token] -------------
+  int row[kBT];
+#pragma unroll
+  for (int q = 0; q < kBT; ++q) {
+    const int j = 16 * q + li;
+    int id = -1;
+    if (j < m) id = (MODE == MODE_LIST) ? s_list[j] : g0 + s_list[j];
+    row[q] = id;
+  }
+  const int kw = d / kBNW, kb = wave * kw;
+  const int t = wave;   // after the sum, thread (t, lane) finishes tile t
+  const int slot = 16 * t + li;
+  const int id = slot < m ? ((MODE == MODE_LIST) ? s_list[slot] : g0 + s_list[slot]) : -1;
+  float bj = 0.f;
+  if (MODE != MODE_EXACT && id >= 0) bj = A.b[id];
+  f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+  if (MODE == MODE_EXACT) {
+    if (A.gated) {
+      const f16* const w[1] = {static_cast<const f16*>(A.w_up)};
+      f32x4 acc[1][kBT];
+      tiles_mma_f16<1>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+#pragma unroll
+      for (int q = 0; q < kBT; ++q) s_red[wave][1][q][lane] = acc[0][q];
+      __syncthreads();
+      if (t < nt) u = wave_tiles_sum(s_red, 1, t, lane);
+    }
+  } else if (A.gated) {
+    const f16* const w[2] = {static_cast<const f16*>(A.w_gate), static_cast<const f16*>(A.w_up)};
+    f32x4 acc[2][kBT];
+    tiles_mma_f16<2>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+#pragma unroll
+    for (int q = 0; q < kBT; ++q) {
+      s_red[wave][0][q][lane] = acc[0][q];
+      s_red[wave][1][q][lane] = acc[1][q];
+    }
+    __syncthreads();
+    if (t < nt) {
+      g = wave_tiles_sum(s_red, 0, t, lane);
+      u = wave_tiles_sum(s_red, 1, t, lane);
+    }
+  } else {
+    const f16* const w[1] = {static_cast<const f16*>(A.w_up)};
+    f32x4 acc[1][kBT];
+    tiles_mma_f16<1>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+#pragma unroll
+    for (int q = 0; q < kBT; ++q) s_red[wave][1][q][lane] = acc[0][q];
+    __syncthreads();
+    if (t < nt) u = wave_tiles_sum(s_red, 1, t, lane);
+  }
+  if (id >= 0 && slot < m) {
+    f32x4 a;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 4 * lk + v;
+      float av;
+      if (MODE == MODE_EXACT) {
+        const float pre = s_pre[s_list[slot] * kMaxTokens + tok];
+        av = A.gated ? fmaxf(pre, 0.f) * u[v] : fmaxf(pre, 0.f);
+      } else {
+        av = A.gated ? fmaxf(g[v] + bj, 0.f) * u[v] : fmaxf(u[v] + bj, 0.f);
+      }
+      a[v] = tok < B ? av : 0.f;
+    }
+    *reinterpret_cast<f32x4*>(abuf + (size_t)id * kMaxTokens + 4 * lk) = a;
+  }
+}
+
+// y partial of neuron chunk blockIdx.y over columns [blockIdx.x * 512, +512): the chunk is a
+// range of mask words (predicted, exact), of neurons (dense) or of list entries (list).
+template <int MODE>
+__global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restrict__ abuf, const f16* __restrict__ wd,
+                                                          const unsigned* __restrict__ mask_words,
+                                                          const int* __restrict__ list, const int* __restrict__ list_count,
+                                                          int n, int d, int B, float* __restrict__ partial) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, li = lane & 15, lk = lane >> 4;
+  const int C = gridDim.y, c = blockIdx.y;
+  const int c0 = blockIdx.x * (kDW * kDCols) + wave * kDCols;
+  const bool cols = c0 < d;   // d is a multiple of 128
+  __shared__ int s_list[kDSeg];
+  __shared__ int s_cnt;
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int lo, hi;   // the chunk, in words (mask modes, dense) or list entries (list)
+  if (MODE == MODE_LIST) {
+    const int cnt = min(max(*list_count, 0), n);
+    lo = (int)((long long)c * cnt / C);
+    hi = (int)((long long)(c + 1) * cnt / C);
+  } else {
+    const int nw = (n + 31) / 32;
+    lo = (int)((long long)c * nw / C);
+    hi = (int)((long long)(c + 1) * nw / C);
+  }
+  constexpr int kSegUnits = (MODE == MODE_LIST) ? kDSeg : kDSeg / 32;
+  for (int s0 = lo; s0 < hi; s0 += kSegUnits) {
+    const int s1 = min(hi, s0 + kSegUnits);
+    __syncthreads();   // the previous segment's list is no longer read
+    if (MODE == MODE_PRED || MODE == MODE_EXACT) {
+      if (wave == 0) {   // 64 lanes, one mask word each: in-wave scan of the popcounts
+        const unsigned word = (s0 + lane < s1) ? mask_words[s0 + lane] : 0u;
+        const int pc = __popc(word);
+        int incl = pc;
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+          const int y = __shfl_up(incl, off, WAVE);
+          if (lane >= off) incl += y;
+        }
+        int pos = incl - pc;
+        unsigned mw = word;
+        while (mw) {
+          const int bit = __ffs((int)mw) - 1;
+          s_list[pos++] = 32 * (s0 + lane) + bit;
+          mw &= mw - 1u;
+        }
+        if (lane == WAVE - 1) s_cnt = incl;
+      }
+    } else if (MODE == MODE_DENSE) {
+      const int first = 32 * s0, last = min(n, 32 * s1);
+      for (int j = threadIdx.x; j < last - first; j += blockDim.x) s_list[j] = first + j;
+      if (threadIdx.x == 0) s_cnt = max(0, last - first);
+    } else {
+      for (int j = threadIdx.x; j < s1 - s0; j += blockDim.x) {
+        const int id = list[s0 + j];
+        s_list[j] = ((unsigned)id < (unsigned)n) ? id : -1;
+      }
+      if (threadIdx.x == 0) s_cnt = s1 - s0;
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    if (!cols) continue;
+    struct DStep {
+      float av[kDU];
+      u32x4 wv[kDU];
+    };
+    auto load = [&](DStep& st, int j0) {
+#pragma unroll
+      for (int q = 0; q < kDU; ++q) {
+        const int j = j0 + 4 * q + lk;
+        const int id = j < cnt ? s_list[j] : -1;
+        st.av[q] = id >= 0 ? abuf[(size_t)id * kMaxTokens + li] : 0.f;
+        st.wv[q] = id >= 0 ? ld_stream(reinterpret_cast<const u32x4*>(wd + (size_t)id * d + c0) + li)
+                           : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto mma = [&](const DStep& st) {
+#pragma unroll
+      for (int q = 0; q < kDU; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = mma_f32(st.av[q], half_at(st.wv[q], e), acc[e]);
+    };
+    constexpr int kStep = 4 * kDU;
+    DStep st0, st1;
+    if (cnt > 0) load(st0, 0);
+    for (int j0 = 0; j0 < cnt; j0 += 2 * kStep) {
+      if (j0 + kStep < cnt) load(st1, j0 + kStep);
+      mma(st0);
+      if (j0 + 2 * kStep < cnt) load(st0, j0 + 2 * kStep);
+      if (j0 + kStep < cnt) mma(st1);
+    }
+  }
+  if (!cols) return;
+  // tile e holds columns c0 + 8 * (lane % 16) + e for tokens 4 * (lane / 16) + v
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int tok = 4 * lk + v;
+    if (tok < B) {
+      float* dst = partial + ((size_t)c * B + tok) * d + c0 + 8 * li;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][v], acc[1][v], acc[2][v], acc[3][v]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4][v], acc[5][v], acc[6][v], acc[7][v]};
+    }
+  }
+}
+
+}  // namespace pik

@@ -503,8 +503,9 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// k_finish: y[t][c] = sum over groups g (in order) of partial[g][t][c]; the
-// extra last workgroup writes the index list (compacted mask words, or 0..n-1).
+// k_finish: y[t][c] = sum over groups g (in order) of partial[g][t][c], one grid row per
+// token; the extra last workgroup of row 0 writes the index list (compacted mask words, or
+// 0..n-1).
 // ---------------------------------------------------------------------------
 template <int OT>
 __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partial, int NG, int B, int d,
@@ -513,6 +514,7 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
                                                 int* __restrict__ count_out, int n_col_blocks) {
   using YT = typename VecT<OT>::T;
   if ((int)blockIdx.x == n_col_blocks) {
+    if (blockIdx.y != 0) return;
     if (mask_words != nullptr) {
       block_compact(mask_words, n_words, idx_out, count_out);
     } else if (iota_n > 0) {
@@ -528,34 +530,33 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
   __shared__ f32x4 s_red[kS][kQ];
   const int cq = threadIdx.x % kQ, sl = threadIdx.x / kQ;
   const int col = blockIdx.x * (4 * kQ) + cq * 4;
-  YT* yo = static_cast<YT*>(y);
-  for (int t = 0; t < B; ++t) {
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    if (col < d) {
-      for (int g0 = sl; g0 < NG; g0 += kS * kU) {
-        f32x4 v[kU];
+  const int t = blockIdx.y;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  if (col < d) {
+    for (int g0 = sl; g0 < NG; g0 += kS * kU) {
+      f32x4 v[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int g = g0 + kS * u;
-          v[u] = g < NG ? *reinterpret_cast<const f32x4*>(partial + ((size_t)g * B + t) * d + col)
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) sum += v[u];
+      for (int u = 0; u < kU; ++u) {
+        const int g = g0 + kS * u;
+        v[u] = g < NG ? *reinterpret_cast<const f32x4*>(partial + ((size_t)g * B + t) * d + col)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) sum += v[u];
     }
-    s_red[sl][cq] = sum;
+  }
+  s_red[sl][cq] = sum;
+  __syncthreads();
+#pragma unroll
+  for (int stride = kS / 2; stride > 0; stride /= 2) {
+    if (sl < stride) s_red[sl][cq] += s_red[sl + stride][cq];
     __syncthreads();
+  }
+  if (sl == 0 && col < d) {
+    const f32x4 tot = s_red[0][cq];
+    YT* yo = static_cast<YT*>(y) + (size_t)t * d + col;
 #pragma unroll
-    for (int stride = kS / 2; stride > 0; stride /= 2) {
-      if (sl < stride) s_red[sl][cq] += s_red[sl + stride][cq];
-      __syncthreads();
-    }
-    if (sl == 0 && col < d) {
-      const f32x4 tot = s_red[0][cq];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) yo[(size_t)t * d + col + e] = from_f32<YT>(tot[e]);
-    }
+    for (int e = 0; e < 4; ++e) yo[e] = from_f32<YT>(tot[e]);
   }
 }
 
@@ -568,6 +569,7 @@ inline hipError_t with_nb(int B, F&& f) {
 
 // Per-weight-format launchers, each compiled in its own translation unit.
 hipError_t launch_ffn_group_f16(int at, int mode, const GroupArgs& a, int cpl, hipStream_t s);
-hipError_t launch_ffn_group_other(int wt, int at, int mode, const GroupArgs& a, int cpl, hipStream_t s);
+hipError_t launch_ffn_group_f32(int at, int mode, const GroupArgs& a, int cpl, hipStream_t s);
+hipError_t launch_ffn_group_q4(int at, int mode, const GroupArgs& a, int cpl, hipStream_t s);
 
 }  // namespace pik

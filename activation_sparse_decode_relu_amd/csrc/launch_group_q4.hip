@@ -1,4 +1,4 @@
-// Group kernel instances for fp32 and int4 weights.
+// Group kernel instances for int4 (group-32) weights.
 #include "kernels_impl.h"
 
 namespace pik {
@@ -24,14 +24,11 @@ namespace pik {
     else PIK_GRP_C(W, AC, MODE_LIST);                          \
   } while (0)
 
-hipError_t launch_ffn_group_other(int wt, int at, int mode, const GroupArgs& a, int cpl, hipStream_t s) {
+hipError_t launch_ffn_group_q4(int at, int mode, const GroupArgs& a, int cpl, hipStream_t s) {
   return with_nb(a.B, [&](auto nbc) -> hipError_t {
     constexpr int NB = decltype(nbc)::value;
-    if (wt == DT_F32 && at == DT_F32) PIK_GRP_M(DT_F32, DT_F32);
-    else if (wt == DT_F32 && at == DT_F16) PIK_GRP_M(DT_F32, DT_F16);
-    else if (wt == DT_Q4 && at == DT_F16) PIK_GRP_M(DT_Q4, DT_F16);
-    else if (wt == DT_Q4 && at == DT_F32) PIK_GRP_M(DT_Q4, DT_F32);
-    else return hipErrorInvalidValue;
+    if (at == DT_F16) PIK_GRP_M(DT_Q4, DT_F16);
+    else PIK_GRP_M(DT_Q4, DT_F32);
     return hipGetLastError();
   });
 }

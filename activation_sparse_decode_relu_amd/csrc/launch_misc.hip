@@ -46,7 +46,8 @@ hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStr
   const int cpl = group_cpl(wt, a.d, a.nw);
   if (cpl == 0) return hipErrorInvalidValue;
   if (wt == DT_F16) return launch_ffn_group_f16(at, mode, a, cpl, s);
-  return launch_ffn_group_other(wt, at, mode, a, cpl, s);
+  if (wt == DT_F32) return launch_ffn_group_f32(at, mode, a, cpl, s);
+  return launch_ffn_group_q4(at, mode, a, cpl, s);
 }
 
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
@@ -55,11 +56,12 @@ hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, voi
   const int ncol = reduce ? (d + 31) / 32 : 0;   // 32 columns per workgroup
   const int grid = ncol + (index_list ? 1 : 0);
   if (grid == 0) return hipSuccess;
+  const dim3 g(grid, reduce ? B : 1);   // one row of column blocks per token
   if (ot == DT_F16)
-    hipLaunchKernelGGL((k_finish<DT_F16>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
+    hipLaunchKernelGGL((k_finish<DT_F16>), g, dim3(kBlock), 0, s, partial, ng, B, d, y,
                        index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
   else
-    hipLaunchKernelGGL((k_finish<DT_F32>), dim3(grid), dim3(kBlock), 0, s, partial, ng, B, d, y,
+    hipLaunchKernelGGL((k_finish<DT_F32>), g, dim3(kBlock), 0, s, partial, ng, B, d, y,
                        index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
   return hipGetLastError();
 }

@@ -33,6 +33,19 @@ PHASES_BY_MODE = {
 }
 
 
+def batched_path(cfg, B: int) -> bool:
+    """Whether the library takes its matrix-core batch path for this workload (same rule as the C side)."""
+    return (1 < B <= 16 and cfg.w_dtype == "f16" and cfg.act_dtype == "f16" and cfg.p_dtype == "f16"
+            and cfg.d_model % 128 == 0 and cfg.rank % 128 == 0)
+
+
+def phases_for(cfg, mode: str, B: int):
+    ph = PHASES_BY_MODE[mode]
+    if batched_path(cfg, B):
+        ph = ph[:-1] + ("down",) + ph[-1:]
+    return ph
+
+
 def esize(dt: str) -> float:
     return {"f32": 4.0, "f16": 2.0}[dt]
 
@@ -72,19 +85,25 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int) -> float:
     pred_hidden: P1, x, h.  group: the mask source (P2 + b_p, or the dense
     pre-activation rows + b), the selected rows of every matrix the mode reads
     with their bias, x and the mask bits; its partial-sum writes are scratch
-    and not counted.  finish: y and the index list.
+    and not counted.  On the batched path the group kernel reads the selected
+    gate/up rows and the down kernel the selected down rows (the activations
+    handed between them are scratch).  finish: y and the index list.
     """
     d, n, r = cfg.d_model, cfg.d_ffn, cfg.rank
     ea, rb = esize(cfg.act_dtype), row_bytes(cfg.w_dtype, d)
+    down = 0 if batched_path(cfg, B) else 1      # down rows read by the group kernel
     if phase == "pred_hidden":
         return r * d * esize(cfg.p_dtype) + B * d * ea + B * r * 4
     if phase == "group":
         xb = B * d * ea + n / 8
         if mode == "predicted":
-            return n * r * esize(cfg.p_dtype) + 4 * n + B * r * 4 + count * ((3 if cfg.gated else 2) * rb + 4) + xb
+            return (n * r * esize(cfg.p_dtype) + 4 * n + B * r * 4 + count * ((1 + down + cfg.gated) * rb + 4)
+                    + xb)
         if mode == "exact":
-            return n * rb + 4 * n + count * ((2 if cfg.gated else 1) * rb) + xb
-        return count * ((3 if cfg.gated else 2) * rb + 4) + xb
+            return n * rb + 4 * n + count * ((down + cfg.gated) * rb) + xb
+        return count * ((1 + down + cfg.gated) * rb + 4) + xb
+    if phase == "down":
+        return count * rb + n / 8
     if phase == "finish":
         return B * d * ea + 4 * count
     raise KeyError(phase)
@@ -187,7 +206,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, 
     f_scale = expect_kib / (sum(big_f) / len(big_f)) if big_f else None
     w_scale = expect_kib / (sum(big_w) / len(big_w)) if big_w else None
     out = {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
-    phase_of = {"k_pred_hidden": "pred_hidden", "k_ffn_group": "group", "k_finish": "finish"}
+    phase_of = {"k_pred_hidden": "pred_hidden", "k_ffn_group": "group", "k_ffn_bgroup": "group",
+                "k_ffn_bdown": "down", "k_finish": "finish"}
     for name, vals in fetch.items():
         phase = next((p for k, p in phase_of.items() if k in name), None)
         if phase is None or f_scale is None:
@@ -361,7 +381,7 @@ def main() -> int:
     # host enqueues one token's L layers, each with an event pair around the phase's kernel.
     phase_stats = {}
     n_prof = min(args.profile_tokens, T)
-    for phase in PHASES_BY_MODE[mode]:
+    for phase in phases_for(cfg, mode, B):
         durs, nbytes = [], []
         for t in range(n_prof):
             starts = [HipEvent() for _ in range(L)]

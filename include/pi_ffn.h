@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PI_FFN_ABI_VERSION 1
+#define PI_FFN_ABI_VERSION 2
 
 typedef enum pi_status {
   PI_OK = 0,
@@ -81,9 +81,13 @@ typedef enum pi_mask_mode {
 /* Kernels a profiling event pair can bracket (pi_ffn_profile_next). */
 typedef enum pi_phase {
   PI_PHASE_PRED_HIDDEN = 0, /* h = ReLU(x P1^T)                                        */
-  PI_PHASE_GROUP = 1,       /* per neuron group: mask, row gather, ReLU(g)*u, partial y */
-  PI_PHASE_FINISH = 2,      /* fixed-order sum of the group partials; index list        */
-  PI_PHASE_COUNT = 3
+  PI_PHASE_GROUP = 1,       /* per neuron group: mask, row gather, ReLU(g)*u, and (one
+                               token, or dtypes the matrix-core path does not take) the
+                               group's partial y                                         */
+  PI_PHASE_DOWN = 2,        /* batched matrix-core path only: partial y over (neuron
+                               chunk, column slice) from the group kernel's activations  */
+  PI_PHASE_FINISH = 3,      /* fixed-order sum of the partials; index list              */
+  PI_PHASE_COUNT = 4
 } pi_phase;
 
 typedef struct pi_ffn_desc {

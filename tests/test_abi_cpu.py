@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(pi.LIB, name), f"{name} is declared in pi_ffn.h but not exported"
     assert set(declared_functions()) == set(pi.EXPORTED)
-    assert pi.LIB.pi_ffn_abi_version() == 1
+    assert pi.LIB.pi_ffn_abi_version() == 2
 
 
 def test_struct_layouts_match_header():
