@@ -40,7 +40,6 @@ constexpr int kBT = kBG / 16;   // 16-neuron tiles per group
 constexpr int kDW = 4;          // waves per down workgroup
 constexpr int kDCols = 128;     // output columns per down wave: 8 MFMA tiles of 16
 constexpr int kDSeg = 2048;     // neurons a down workgroup compacts into LDS at a time
-constexpr int kDU = 8;          // 4-neuron steps per down iteration
 
 // D[16][16] += A[16][4] B[4][16] (fp32): lane l gives A[l%16][l/16] and B[l/16][l%16] and
 // holds D[4(l/16)+v][l%16] in element v.
@@ -305,6 +304,15 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
 
 // y partial of neuron chunk blockIdx.y over columns [blockIdx.x * 512, +512): the chunk is a
 // range of mask words (predicted, exact), of neurons (dense) or of list entries (list).
+// Steps of kDStep neurons: the workgroup reads each neuron's 1 KB row segment with one
+// row-contiguous load (the pattern HBM streams best), stages the step in LDS, and each wave
+// then reads its 128 columns back in the MFMA layout.  Two LDS buffers: the next step's rows
+// are in flight while the current step is multiplied.
+constexpr int kDStep = 32;                 // neurons per down step (two workgroups fit a CU's LDS)
+constexpr int kDRow = kDW * kDCols;        // 512 columns: a 1 KB fp16 row segment
+constexpr int kDPitch = kDRow + 8;         // LDS row pitch in halves (rows start 16 bytes apart in bank order)
+constexpr int kDRowsPerWave = kDStep / kDW;
+
 template <int MODE>
 __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restrict__ abuf, const f16* __restrict__ wd,
                                                           const unsigned* __restrict__ mask_words,
@@ -312,10 +320,13 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
                                                           int n, int d, int B, float* __restrict__ partial) {
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, li = lane & 15, lk = lane >> 4;
   const int C = gridDim.y, c = blockIdx.y;
-  const int c0 = blockIdx.x * (kDW * kDCols) + wave * kDCols;
-  const bool cols = c0 < d;   // d is a multiple of 128
+  const int cw = blockIdx.x * kDRow;               // first column of the workgroup's slice
+  const int ncols = min(kDRow, d - cw);            // a multiple of 128
+  const bool cols = wave * kDCols < ncols;         // this wave's 128 columns exist
   __shared__ int s_list[kDSeg];
   __shared__ int s_cnt;
+  __shared__ f16 s_w[2][kDStep][kDPitch];
+  __shared__ float s_a[2][kDStep][kMaxTokens];
 
   f32x4 acc[8];
 #pragma unroll
@@ -331,10 +342,16 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
     lo = (int)((long long)c * nw / C);
     hi = (int)((long long)(c + 1) * nw / C);
   }
+  // one step in registers: this wave's kDRowsPerWave rows (16 bytes per lane) and, for the first
+  // 128 threads, 4 tokens' activations of one neuron
+  struct DRegs {
+    u32x4 w[kDRowsPerWave];
+    f32x4 a;
+  };
   constexpr int kSegUnits = (MODE == MODE_LIST) ? kDSeg : kDSeg / 32;
   for (int s0 = lo; s0 < hi; s0 += kSegUnits) {
     const int s1 = min(hi, s0 + kSegUnits);
-    __syncthreads();   // the previous segment's list is no longer read
+    __syncthreads();   // the previous segment's list and buffers are no longer read
     if (MODE == MODE_PRED || MODE == MODE_EXACT) {
       if (wave == 0) {   // 64 lanes, one mask word each: in-wave scan of the popcounts
         const unsigned word = (s0 + lane < s1) ? mask_words[s0 + lane] : 0u;
@@ -367,39 +384,57 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
     }
     __syncthreads();
     const int cnt = s_cnt;
-    if (!cols) continue;
-    struct DStep {
-      float av[kDU];
-      u32x4 wv[kDU];
-    };
-    auto load = [&](DStep& st, int j0) {
+    auto load = [&](DRegs& r, int j0) {
 #pragma unroll
-      for (int q = 0; q < kDU; ++q) {
-        const int j = j0 + 4 * q + lk;
+      for (int i = 0; i < kDRowsPerWave; ++i) {
+        const int j = j0 + wave * kDRowsPerWave + i;
         const int id = j < cnt ? s_list[j] : -1;
-        st.av[q] = id >= 0 ? abuf[(size_t)id * kMaxTokens + li] : 0.f;
-        st.wv[q] = id >= 0 ? ld_stream(reinterpret_cast<const u32x4*>(wd + (size_t)id * d + c0) + li)
-                           : u32x4{0, 0, 0, 0};
+        r.w[i] = (id >= 0 && 8 * lane < ncols)
+                     ? ld_stream(reinterpret_cast<const u32x4*>(wd + (size_t)id * d + cw) + lane)
+                     : u32x4{0, 0, 0, 0};
+      }
+      r.a = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (threadIdx.x < kDStep * 4) {
+        const int j = j0 + (int)threadIdx.x / 4;
+        const int id = j < cnt ? s_list[j] : -1;
+        if (id >= 0) r.a = *reinterpret_cast<const f32x4*>(abuf + (size_t)id * kMaxTokens + 4 * (threadIdx.x % 4));
       }
     };
-    auto mma = [&](const DStep& st) {
+    auto stage = [&](const DRegs& r, int buf) {
 #pragma unroll
-      for (int q = 0; q < kDU; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = mma_f32(st.av[q], half_at(st.wv[q], e), acc[e]);
+      for (int i = 0; i < kDRowsPerWave; ++i)
+        *reinterpret_cast<u32x4*>(&s_w[buf][wave * kDRowsPerWave + i][8 * lane]) = r.w[i];
+      if (threadIdx.x < kDStep * 4)
+        *reinterpret_cast<f32x4*>(&s_a[buf][threadIdx.x / 4][4 * (threadIdx.x % 4)]) = r.a;
     };
-    constexpr int kStep = 4 * kDU;
-    DStep st0, st1;
-    if (cnt > 0) load(st0, 0);
-    for (int j0 = 0; j0 < cnt; j0 += 2 * kStep) {
-      if (j0 + kStep < cnt) load(st1, j0 + kStep);
-      mma(st0);
-      if (j0 + 2 * kStep < cnt) load(st0, j0 + 2 * kStep);
-      if (j0 + kStep < cnt) mma(st1);
+    auto mma = [&](int buf) {
+      if (!cols) return;
+#pragma unroll
+      for (int q = 0; q < kDStep / 4; ++q) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&s_w[buf][4 * q + lk][wave * kDCols + 8 * li]);
+        const float a = s_a[buf][4 * q + lk][li];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = mma_f32(a, half_at(w, e), acc[e]);
+      }
+    };
+    if (cnt == 0) continue;
+    DRegs r;
+    load(r, 0);
+    stage(r, 0);
+    __syncthreads();
+    int buf = 0;
+    for (int j0 = 0; j0 < cnt; j0 += kDStep) {
+      const bool more = j0 + kDStep < cnt;   // uniform
+      if (more) load(r, j0 + kDStep);
+      mma(buf);
+      if (more) stage(r, buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
   }
   if (!cols) return;
-  // tile e holds columns c0 + 8 * (lane % 16) + e for tokens 4 * (lane / 16) + v
+  // tile e holds columns cw + 128 * wave + 8 * (lane % 16) + e for tokens 4 * (lane / 16) + v
+  const int c0 = cw + wave * kDCols;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int tok = 4 * lk + v;

@@ -12,7 +12,8 @@ int batch_groups(int n) { return (n + kBG - 1) / kBG; }
 
 int batch_down_chunks(int d) {
   const int slices = (d + kDW * kDCols - 1) / (kDW * kDCols);
-  return (256 + slices - 1) / slices;   // about 256 down workgroups
+  return (512 + slices - 1) / slices;   // about 512 down workgroups: two per CU, so one can multiply
+                                        // while the other waits on its rows
 }
 
 hipError_t launch_ffn_bgroup(int mode, const GroupArgs& a, float* abuf, hipStream_t s) {
