@@ -84,6 +84,7 @@ Layout layout_for(const pi_ffn_desc& d) {
   // partials: one [B][d] block per group workgroup, or per down chunk on the batched path
   L.max_partials = L.n_groups;
   if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
+  L.max_partials = std::max(L.max_partials, pik::wave_grid(d.d_ffn));
   L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.max_partials * B * dm);
   L.total = off;
   return L;
@@ -244,6 +245,10 @@ pi_status group_phase(pi_ffn* h, int mode, const pik::GroupArgs& a, hipStream_t 
     *partials = chunks;
     return run_phase(h, PI_PHASE_DOWN, s, "ffn_bdown",
                      [&] { return pik::launch_ffn_bdown(mode, a, h->abuf(), chunks, s); });
+  }
+  if (pik::wave_supported(d.w_dtype, d.act_dtype, d.p_dtype, mode, a.B, d.d_model)) {
+    *partials = pik::wave_grid(d.d_ffn);
+    return run_phase(h, PI_PHASE_GROUP, s, "ffn_wave", [&] { return pik::launch_ffn_wave(a, s); });
   }
   *partials = h->L.n_groups;
   return run_phase(h, PI_PHASE_GROUP, s, "ffn_group",

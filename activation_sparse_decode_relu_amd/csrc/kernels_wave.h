@@ -1,0 +1,155 @@
+// The one-token predicted step with wave-independent neuron ownership (fp16 weights,
+// activations and predictor, d = 512 * CPLF up to 4096).
+//
+// A workgroup owns a byte-aligned range of about n / (#CUs) neurons, one workgroup per CU, and
+// splits it into 8 waves of at most kWRows consecutive neurons.  Each wave, on its own:
+//   mask    its rows' predictor logits z = h P2^T + b_p (1 KB row-contiguous loads), the
+//           threshold, and a ballot of its decisions;
+//   gather  for each of its selected neurons in order, the full gate / up / down rows, the
+//           activation a = ReLU(x W_gate + b) * (x W_up) from two wave sums, and
+//           y += a * W_down^T row over the full d, in registers.
+// There is no barrier between a wave's mask and gather phases, so the waves of a CU drift
+// apart and the CU streams predictor rows and gathered rows at the same time instead of in
+// two workgroup-wide phases.  At the end, each wave that selected something stores its y in
+// its own LDS slot (a wave that selected nothing holds an exact +0 vector and stores nothing);
+// after one barrier every thread adds the occupied slots in wave order into the workgroup's
+// partial, so the result is the same on every run.
+// The step is the PowerInfer paper explainer's FFN equation (section
+// "ニューロン活性化のべき乗則分布") over the neurons its predictor (section "活性化予測器")
+// selects (section "GPU-CPUハイブリッドアーキテクチャ", inference flow).
+#pragma once
+
+#include "kernels_impl.h"
+
+namespace pik {
+
+constexpr int kWWaves = 8;   // waves per workgroup
+constexpr int kWRows = 8;    // most neurons one wave owns (a workgroup owns at most 64)
+
+template <int CPLF>
+__global__ __launch_bounds__(kWWaves * WAVE) void k_ffn_wave(const GroupArgs A, int n_units) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int n = A.n, d = A.d, r = A.r;
+  // this workgroup's neurons: 8-neuron units [u0, u1), so its mask bits are whole bytes
+  const int u0 = (int)((long long)blockIdx.x * n_units / gridDim.x);
+  const int u1 = (int)((long long)(blockIdx.x + 1) * n_units / gridDim.x);
+  const int r0 = 8 * u0, r1 = min(n, 8 * u1);
+  const int rpw = (r1 - r0 + kWWaves - 1) / kWWaves;   // <= kWRows
+  const int w0 = r0 + wave * rpw, w1 = min(r1, w0 + rpw);
+
+  __shared__ unsigned s_bits[2];                    // the workgroup's decisions (at most 64 neurons)
+  __shared__ unsigned s_busy;                       // bit w: wave w selected a neuron and stored its y
+  __shared__ f32x4 s_y[kWWaves][CPLF * WAVE * 2];   // each wave's y, 8 floats per 16-byte chunk
+
+  if (threadIdx.x < 2) s_bits[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) s_busy = 0u;
+  __syncthreads();
+
+  // ---- mask: this wave's rows ------------------------------------------------------------------
+  float row_bias = 0.f;
+  if (lane < w1 - w0) row_bias = A.b_p[w0 + lane];
+  int rows[kWRows];
+#pragma unroll
+  for (int j = 0; j < kWRows; ++j) rows[j] = (w0 + j < w1) ? w0 + j : -1;
+  float zacc[kWRows][1];
+  rows_dot<DT_F16, DT_F32, 1, kWRows, 2>(zacc, static_cast<const char*>(A.p2), row_bytes(DT_F16, r), nullptr, r, rows,
+                                          A.h, 0, 1);
+  unsigned mine = 0u;   // bit j: row w0 + j selected (wave-uniform)
+#pragma unroll
+  for (int j = 0; j < kWRows; ++j) {
+    const float v = wave_sum(zacc[j][0]) +
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, row_bias), j));
+    if (rows[j] >= 0) {
+      if (A.logits != nullptr && lane == 0) A.logits[rows[j]] = v;
+      if (v > A.thr) mine |= 1u << j;
+    }
+  }
+
+  // ---- gather: this wave's selected neurons, full rows, y over the full d ----------------------
+  constexpr int NE = 8;
+  float acc[CPLF][NE];
+#pragma unroll
+  for (int q = 0; q < CPLF; ++q)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[q][e] = 0.f;
+  if (!A.mask_only && mine != 0u) {
+    const f16* xb = static_cast<const f16*>(A.x);
+    XChunk<DT_F16, DT_F16> xq[CPLF];
+#pragma unroll
+    for (int q = 0; q < CPLF; ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * 8);
+    const size_t rbytes = row_bytes(DT_F16, d);
+    const char* wgb = static_cast<const char*>(A.w_gate);
+    const char* wub = static_cast<const char*>(A.w_up);
+    const char* wdb = static_cast<const char*>(A.w_down_t);
+    unsigned todo = mine;
+    while (todo != 0u) {
+      const int j = __ffs((int)todo) - 1;
+      todo &= todo - 1u;
+      const int id = w0 + j;
+      const float bj = A.b[id];
+      u32x4 wg[CPLF], wu[CPLF], wd[CPLF];
+#pragma unroll
+      for (int q = 0; q < CPLF; ++q) {
+        const int c = lane + q * WAVE;
+        wg[q] = A.gated ? ld_stream(reinterpret_cast<const u32x4*>(wgb + rbytes * id) + c) : u32x4{0, 0, 0, 0};
+        wu[q] = ld_stream(reinterpret_cast<const u32x4*>(wub + rbytes * id) + c);
+        wd[q] = ld_stream(reinterpret_cast<const u32x4*>(wdb + rbytes * id) + c);
+      }
+      float pg = 0.f, pu = 0.f;
+#pragma unroll
+      for (int q = 0; q < CPLF; ++q) {
+        if (A.gated) dot_chunk<DT_F16, DT_F16>(pg, wg[q], xq[q], 1.f);
+        dot_chunk<DT_F16, DT_F16>(pu, wu[q], xq[q], 1.f);
+      }
+      const float g = A.gated ? wave_sum(pg) : 0.f;
+      const float u = wave_sum(pu);
+      const float a = A.gated ? fmaxf(g + bj, 0.f) * u : fmaxf(u + bj, 0.f);
+#pragma unroll
+      for (int q = 0; q < CPLF; ++q) {
+        float wf[NE];
+        Unpack<DT_F16>::run(wd[q], wf);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[q][e] = fmaf(a, wf[e], acc[q][e]);
+      }
+    }
+  }
+
+  // ---- the workgroup's mask bytes and partial of y ---------------------------------------------
+  if (lane == 0 && mine != 0u) {
+    const int off = w0 - r0;   // < 64
+    atomicOr(&s_bits[off / 32], mine << (off % 32));
+    if (off % 32 + rpw > 32) atomicOr(&s_bits[off / 32 + 1], mine >> (32 - off % 32));
+  }
+  if (!A.mask_only && mine != 0u) {
+#pragma unroll
+    for (int q = 0; q < CPLF; ++q) {
+      const int c = lane + q * WAVE;
+      s_y[wave][2 * c] = f32x4{acc[q][0], acc[q][1], acc[q][2], acc[q][3]};
+      s_y[wave][2 * c + 1] = f32x4{acc[q][4], acc[q][5], acc[q][6], acc[q][7]};
+    }
+    if (lane == 0) atomicOr(&s_busy, 1u << wave);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < u1 - u0) {
+    const int bo = 8 * (int)threadIdx.x;
+    reinterpret_cast<unsigned char*>(A.mask_words)[u0 + threadIdx.x] =
+        (unsigned char)(s_bits[bo / 32] >> (bo % 32));
+  }
+  if (A.mask_only) return;
+  const unsigned busy = s_busy;
+  float* dst = A.partial + (size_t)blockIdx.x * d;
+  for (int k = threadIdx.x; k < CPLF * WAVE * 2; k += blockDim.x) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    bool first = true;
+#pragma unroll
+    for (int w = 0; w < kWWaves; ++w) {
+      if ((busy >> w) & 1u) {
+        v = first ? s_y[w][k] : v + s_y[w][k];
+        first = false;
+      }
+    }
+    *reinterpret_cast<f32x4*>(dst + 4 * k) = v;
+  }
+}
+
+}  // namespace pik

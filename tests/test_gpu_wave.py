@@ -1,0 +1,114 @@
+"""GPU parity of the wave-independent one-token predicted kernel (fp16 weights,
+activations and predictor, batch 1, d a multiple of 512 up to 4096) against the
+CPU oracle.
+
+Integer-lattice layers make every sum exact, so the index list, the logits and
+y must match the oracle bit for bit.  Shapes cover workgroups of one 8-neuron
+unit (small n), of 5-6 units (n spread over 256 workgroups) and of the
+64-neuron maximum (n large enough that 256 workgroups would not suffice), and
+d from 512 to 4096 including a non-power-of-two multiple of 512.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import config_by_name, make_lattice_layer, make_lattice_tokens, make_layer, make_tokens
+
+from gpu_util import announce, check_decisions, check_idx_valid, rel_l2_rows, run_forward, run_predict
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import activation_sparse_decode_relu_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _pi():
+    import activation_sparse_decode_relu_amd as pi
+    return pi
+
+
+def _bitwise(a, b):
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+@pytest.mark.parametrize("d,n,r,gated", [
+    (512, 1000, 128, True),      # 125 units: one unit per workgroup, ragged last unit
+    (1536, 11000, 256, False),   # 1375 units over 256 workgroups (5-6 units each)
+    (4096, 11008, 1024, True),   # the LLaMA-7B shape
+    (2048, 20000, 64, True),     # 2500 units: 313 workgroups of 7-8 units (64 neurons)
+])
+def test_lattice_bit_exact_wave(d, n, r, gated):
+    announce(f"wave kernel lattice d={d} n={n} r={r} gated={gated}")
+    layer = make_lattice_layer(d, n, r, gated, seed=d + n)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    for t in range(3):
+        x = make_lattice_tokens(d, 1, seed=50 + t)
+        ref = oracle.forward(layer, x, "predicted")
+        idx, count, y = run_forward(h, x, "predicted")
+        check_idx_valid(idx, count, n)
+        assert count == ref["count"] and np.array_equal(idx, ref["idx"]), f"token {t}"
+        assert _bitwise(y, ref["y"]), f"token {t}: y differs bitwise"
+        pidx, _, z = run_predict(h, x)
+        assert np.array_equal(pidx, ref["idx"])
+        assert np.array_equal(z.astype(np.float64), ref["z"])
+    h.close()
+
+
+def test_lattice_wave_nothing_selected():
+    """Every logit below the threshold: the list is empty and y is +0.0."""
+    d, n, r = 1024, 3000, 128
+    announce("wave kernel: no neuron selected")
+    layer = make_lattice_layer(d, n, r, True, seed=77)
+    layer.b_p = np.full(n, -1000.0, dtype=np.float32)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    x = make_lattice_tokens(d, 1, seed=78)
+    idx, count, y = run_forward(h, x, "predicted")
+    assert count == 0
+    assert np.all(y == 0) and not np.signbit(y).any()
+    h.close()
+
+
+def test_random_llama7b_layer_wave_and_graph_replay():
+    cfg = config_by_name("llama7b")
+    announce("wave kernel: random LLaMA-7B layer, guard-band parity and graph replay")
+    layer = make_layer(cfg, 3)
+    pi = _pi()
+    h = pi.upload_layer(layer, "cuda", max_batch=1)
+    x = make_tokens(cfg, 3, 1, start=11)
+    idx, count, y = run_forward(h, x, "predicted")
+    check_idx_valid(idx, count, layer.d_ffn)
+    zo = oracle.predictor_logits(x, layer.p1, layer.p2, layer.b_p)
+    band = oracle.guard_band_predictor(x, layer.p1, layer.p2, layer.b_p)
+    check_decisions(idx, layer.d_ffn, zo, band, oracle.threshold_logit(layer.tau))
+    ref = oracle.forward_masked(layer, x, idx)["y64"]
+    assert rel_l2_rows(y, ref).max() <= 1e-3
+    xt = torch.from_numpy(x).cuda()
+    yt = torch.empty_like(xt)
+    it = torch.empty(layer.d_ffn, dtype=torch.int32, device="cuda")
+    ct = torch.empty(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        h.forward(xt, yt, "predicted", it, ct)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            h.forward(xt, yt, "predicted", it, ct)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        yt.fill_(float("nan"))
+        ct.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert _bitwise(yt.cpu().numpy(), y), f"replay {rep}"
+        assert int(ct.item()) == count and np.array_equal(it[:count].cpu().numpy(), idx)
+        h.forward(xt, yt, "exact")   # eager work (the vector kernel) between replays
+        torch.cuda.synchronize()
+    h.close()
