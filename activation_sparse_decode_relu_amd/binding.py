@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_E
 
 EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",
             "pi_ffn_destroy", "pi_ffn_predict", "pi_ffn_forward", "pi_ffn_forward_masked",
-            "pi_ffn_profile_next")
+            "pi_ffn_launch_plan", "pi_ffn_profile_next")
 
 
 class PiDesc(ctypes.Structure):
@@ -73,6 +73,8 @@ def _load() -> ctypes.CDLL:
     lib.pi_ffn_forward.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
     lib.pi_ffn_forward_masked.restype = st
     lib.pi_ffn_forward_masked.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.pi_ffn_launch_plan.restype = st
+    lib.pi_ffn_launch_plan.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_uint32)]
     lib.pi_ffn_profile_next.restype = st
     lib.pi_ffn_profile_next.argtypes = [vp, i32, vp, vp]
     return lib
@@ -163,6 +165,13 @@ class FFNLayer:
     def forward_masked(self, x, idx, count, y, stream=None) -> None:
         check(LIB.pi_ffn_forward_masked(self.handle, _ptr(x), int(x.shape[0]), _ptr(idx), _ptr(count),
                                         _ptr(y), _stream(stream)))
+
+    def launch_plan(self, batch: int, mode="predicted"):
+        """The phases a forward call with this batch and mode launches, in launch order."""
+        m = MODES[mode] if isinstance(mode, str) else int(mode)
+        out = ctypes.c_uint32(0)
+        check(LIB.pi_ffn_launch_plan(self.handle, int(batch), m, ctypes.byref(out)))
+        return tuple(name for name, p in sorted(PHASES.items(), key=lambda kv: kv[1]) if out.value & (1 << p))
 
     def profile_next(self, phase, start_event, stop_event) -> None:
         p = PHASES[phase] if isinstance(phase, str) else int(phase)

@@ -226,6 +226,20 @@ pik::GroupArgs group_args(const pi_ffn* h, const void* x, int B) {
   return a;
 }
 
+// Which kernels a call runs.
+struct Plan {
+  bool batched;   // matrix-core batch path: group + down kernels
+  bool wave;      // wave-independent one-token kernel
+};
+
+Plan plan_for(const pi_ffn* h, int mode, int B) {
+  const pi_ffn_desc& d = h->desc;
+  Plan p{};
+  p.batched = pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank);
+  p.wave = !p.batched && pik::wave_supported(d.w_dtype, d.act_dtype, d.p_dtype, mode, B, d.d_model);
+  return p;
+}
+
 pi_status hidden_phase(pi_ffn* h, const void* x, int B, hipStream_t s) {
   const pi_ffn_desc& d = h->desc;
   return run_phase(h, PI_PHASE_PRED_HIDDEN, s, "pred_hidden", [&] {
@@ -235,9 +249,9 @@ pi_status hidden_phase(pi_ffn* h, const void* x, int B, hipStream_t s) {
 
 // Runs the group kernel (and, on the batched matrix-core path, the down kernel) for this
 // call; *partials receives the number of partials of y written.
-pi_status group_phase(pi_ffn* h, int mode, const pik::GroupArgs& a, hipStream_t s, int* partials) {
+pi_status group_phase(pi_ffn* h, int mode, const Plan& plan, const pik::GroupArgs& a, hipStream_t s, int* partials) {
   const pi_ffn_desc& d = h->desc;
-  if (pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, a.B, d.d_model, d.rank)) {
+  if (plan.batched) {
     pi_status st = run_phase(h, PI_PHASE_GROUP, s, "ffn_bgroup",
                              [&] { return pik::launch_ffn_bgroup(mode, a, h->abuf(), s); });
     if (st != PI_OK || a.mask_only) return st;
@@ -246,9 +260,10 @@ pi_status group_phase(pi_ffn* h, int mode, const pik::GroupArgs& a, hipStream_t 
     return run_phase(h, PI_PHASE_DOWN, s, "ffn_bdown",
                      [&] { return pik::launch_ffn_bdown(mode, a, h->abuf(), chunks, s); });
   }
-  if (pik::wave_supported(d.w_dtype, d.act_dtype, d.p_dtype, mode, a.B, d.d_model)) {
+  if (plan.wave) {
     *partials = pik::wave_grid(d.d_ffn);
-    return run_phase(h, PI_PHASE_GROUP, s, "ffn_wave", [&] { return pik::launch_ffn_wave(a, s); });
+    return run_phase(h, PI_PHASE_GROUP, s, "ffn_wave",
+                     [&] { return pik::launch_ffn_wave(a, s); });
   }
   *partials = h->L.n_groups;
   return run_phase(h, PI_PHASE_GROUP, s, "ffn_group",
@@ -335,8 +350,9 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, 
   a.logits = logits_dbg;
   a.mask_only = 1;
   int partials = 0;
+  const Plan plan = plan_for(h, pik::MODE_PRED, batch);
   if ((st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
-  if ((st = group_phase(h, pik::MODE_PRED, a, s, &partials)) != PI_OK) return st;
+  if ((st = group_phase(h, pik::MODE_PRED, plan, a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, nullptr, false, 1, idx, count, s)) != PI_OK) return st;
   return ok();
 }
@@ -373,8 +389,9 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
       return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
   }
   int partials = 0;
+  const Plan plan = plan_for(h, mode, batch);
   if (mode == pik::MODE_PRED && (st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
-  if ((st = group_phase(h, mode, a, s, &partials)) != PI_OK) return st;
+  if ((st = group_phase(h, mode, plan, a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
   return ok();
 }
@@ -390,8 +407,30 @@ pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const i
   a.list = idx;
   a.list_count = count;
   int partials = 0;
-  if ((st = group_phase(h, pik::MODE_LIST, a, s, &partials)) != PI_OK) return st;
+  if ((st = group_phase(h, pik::MODE_LIST, plan_for(h, pik::MODE_LIST, batch), a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, y, true, 0, nullptr, nullptr, s)) != PI_OK) return st;
+  return ok();
+}
+
+pi_status pi_ffn_launch_plan(const pi_ffn* h, int32_t batch, int32_t mask_mode, uint32_t* plan) {
+  if (h == nullptr || plan == nullptr) return fail(PI_ERR_INVALID, "handle or plan is NULL");
+  if (batch < 1 || batch > h->desc.max_batch)
+    return fail(PI_ERR_INVALID, "batch=%d must lie in [1, max_batch=%d]", batch, h->desc.max_batch);
+  int mode;
+  switch (mask_mode) {
+    case PI_MASK_PREDICTED:
+      if (h->desc.rank == 0) return fail(PI_ERR_INVALID, "PREDICTED mode needs a predictor (rank > 0)");
+      mode = pik::MODE_PRED;
+      break;
+    case PI_MASK_EXACT_RELU: mode = pik::MODE_EXACT; break;
+    case PI_MASK_DENSE: mode = pik::MODE_DENSE; break;
+    default: return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
+  }
+  const Plan p = plan_for(h, mode, batch);
+  uint32_t bits = (1u << PI_PHASE_GROUP) | (1u << PI_PHASE_FINISH);
+  if (mode == pik::MODE_PRED) bits |= 1u << PI_PHASE_PRED_HIDDEN;
+  if (p.batched) bits |= 1u << PI_PHASE_DOWN;
+  *plan = bits;
   return ok();
 }
 

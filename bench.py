@@ -26,26 +26,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "sparse-FFN decode layers/s + effective HBM GB/s on active-neuron bytes"
-PHASES_BY_MODE = {
-    "predicted": ("pred_hidden", "group", "finish"),
-    "exact": ("group", "finish"),
-    "dense": ("group", "finish"),
-}
-
-
-def batched_path(cfg, B: int) -> bool:
-    """Whether the library takes its matrix-core batch path for this workload (same rule as the C side)."""
-    return (1 < B <= 16 and cfg.w_dtype == "f16" and cfg.act_dtype == "f16" and cfg.p_dtype == "f16"
-            and cfg.d_model % 128 == 0 and cfg.rank % 128 == 0)
-
-
-def phases_for(cfg, mode: str, B: int):
-    ph = PHASES_BY_MODE[mode]
-    if batched_path(cfg, B):
-        ph = ph[:-1] + ("down",) + ph[-1:]
-    return ph
-
-
 def esize(dt: str) -> float:
     return {"f32": 4.0, "f16": 2.0}[dt]
 
@@ -79,7 +59,7 @@ def step_bytes(cfg, mode: str, B: int, count: int) -> float:
     return count * (rows + 4) + io
 
 
-def phase_bytes(cfg, mode: str, phase: str, B: int, count: int) -> float:
+def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases) -> float:
     """Algorithmic bytes one launch of a phase's kernel moves.
 
     pred_hidden: P1, x, h.  group: the mask source (P2 + b_p, or the dense
@@ -88,12 +68,14 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int) -> float:
     and not counted.  On the batched path the group kernel reads the selected
     gate/up rows and the down kernel the selected down rows (the activations
     handed between them are scratch).  finish: y and the index list.
+    `phases` is the library's launch plan for the call.
     """
     d, n, r = cfg.d_model, cfg.d_ffn, cfg.rank
     ea, rb = esize(cfg.act_dtype), row_bytes(cfg.w_dtype, d)
-    down = 0 if batched_path(cfg, B) else 1      # down rows read by the group kernel
+    down = 0 if "down" in phases else 1      # down rows read by the group kernel
+    hidden = r * d * esize(cfg.p_dtype) + B * d * ea + B * r * 4
     if phase == "pred_hidden":
-        return r * d * esize(cfg.p_dtype) + B * d * ea + B * r * 4
+        return hidden
     if phase == "group":
         xb = B * d * ea + n / 8
         if mode == "predicted":
@@ -381,7 +363,8 @@ def main() -> int:
     # host enqueues one token's L layers, each with an event pair around the phase's kernel.
     phase_stats = {}
     n_prof = min(args.profile_tokens, T)
-    for phase in phases_for(cfg, mode, B):
+    plan = handles[0].launch_plan(B, mode)
+    for phase in plan:
         durs, nbytes = [], []
         for t in range(n_prof):
             starts = [HipEvent() for _ in range(L)]
@@ -394,7 +377,7 @@ def main() -> int:
             torch.cuda.synchronize()
             for l in range(L):
                 durs.append(starts[l].elapsed_ms(stops[l]) * 1e-3)
-                nbytes.append(phase_bytes(cfg, mode, phase, B, int(cnt[t, l])))
+                nbytes.append(phase_bytes(cfg, mode, phase, B, int(cnt[t, l]), plan))
         tot_s = sum(durs)
         phase_stats[phase] = {"avg_us": 1e6 * tot_s / len(durs), "min_us": 1e6 * min(durs),
                               "launches": len(durs),

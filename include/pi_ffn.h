@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PI_FFN_ABI_VERSION 2
+#define PI_FFN_ABI_VERSION 3
 
 typedef enum pi_status {
   PI_OK = 0,
@@ -166,6 +166,14 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
  */
 pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx,
                                 const int32_t* count, void* y, void* stream);
+
+/*
+ * Which kernels pi_ffn_forward(h, x, batch, mask_mode, ...) launches, for profiling and
+ * byte accounting: bit p of *plan is set when phase p's kernel runs (pi_phase).  Host
+ * only; enqueues nothing.  Returns PI_ERR_INVALID for a NULL handle or plan, a batch
+ * outside [1, max_batch], an unknown mask mode, or PREDICTED without a predictor.
+ */
+pi_status pi_ffn_launch_plan(const pi_ffn* h, int32_t batch, int32_t mask_mode, uint32_t* plan);
 
 /*
  * Profiling: arm a one-shot event pair.  The next launch of `phase`'s kernel

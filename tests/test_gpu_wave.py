@@ -112,3 +112,15 @@ def test_random_llama7b_layer_wave_and_graph_replay():
         h.forward(xt, yt, "exact")   # eager work (the vector kernel) between replays
         torch.cuda.synchronize()
     h.close()
+
+
+def test_launch_plan_reports_the_kernels():
+    pi = _pi()
+    announce("launch plans of the one-token, batched and vector paths")
+    big = make_lattice_layer(4096, 11008, 1024, True, seed=1)
+    h = pi.upload_layer(big, "cuda", max_batch=16)
+    assert h.launch_plan(1, "predicted") == ("pred_hidden", "group", "finish")
+    assert h.launch_plan(4, "predicted") == ("pred_hidden", "group", "down", "finish")
+    assert h.launch_plan(1, "exact") == ("group", "finish")
+    assert h.launch_plan(16, "dense") == ("group", "down", "finish")
+    h.close()
