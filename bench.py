@@ -189,7 +189,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, 
     w_scale = expect_kib / (sum(big_w) / len(big_w)) if big_w else None
     out = {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     phase_of = {"k_pred_hidden": "pred_hidden", "k_ffn_group": "group", "k_ffn_bgroup": "group",
-                "k_ffn_bdown": "down", "k_finish": "finish"}
+                "k_ffn_wave": "group", "k_ffn_bdown": "down", "k_finish": "finish"}
     for name, vals in fetch.items():
         phase = next((p for k, p in phase_of.items() if k in name), None)
         if phase is None or f_scale is None:
