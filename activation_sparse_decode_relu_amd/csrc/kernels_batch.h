@@ -56,55 +56,51 @@ __device__ __forceinline__ float half_at(u32x4 w, int e) { return (float)__built
 
 // Partial tiles over this wave's share [k_begin, k_end) of a contraction of length K:
 // acc[m][t] += X[tok][k] * W_m[row[t]][k] for the nt tiles in use; rows < 0, tokens >= B and
-// k >= k_end contribute zeros.  MFMA k-steps of 32, double-buffered: the loads of the next
-// step are issued before the products of the current one.
-template <int NM>
-struct F16Step {
-  u32x4 xa, wv[NM][kBT];
-};
+// k >= k_end contribute zeros.  Each batch of loads covers BS consecutive MFMA k-steps of every
+// row in use, so a row is requested 64 * BS contiguous bytes at a time rather than 64: operand
+// tiles read in longer row runs stream markedly faster.
+constexpr int kBS = 4;   // MFMA k-steps (of 32) per load batch
 
-template <int NM>
-__device__ __forceinline__ void f16_step_load(F16Step<NM>& b, const f16* const (&w)[NM], const int (&row)[kBT], int nt,
-                                              const f16* xr, bool xok, int K, int k0, int k_end) {
-  const int kk = k0 + 8 * ((threadIdx.x & (WAVE - 1)) >> 4);
-  const bool ok = k0 < k_end;
-  b.xa = (xok && ok) ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int t = 0; t < kBT; ++t)
-      b.wv[m][t] = (ok && t < nt && row[t] >= 0)
-                       ? ld_stream(reinterpret_cast<const u32x4*>(w[m] + (size_t)row[t] * K + kk))
-                       : u32x4{0, 0, 0, 0};
-}
-
-template <int NM>
-__device__ __forceinline__ void f16_step_mma(f32x4 (&acc)[NM][kBT], const F16Step<NM>& b, int nt) {
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int t = 0; t < kBT; ++t)
-      if (t < nt) acc[m][t] = mma_f16(b.xa, b.wv[m][t], acc[m][t]);
-}
-
-template <int NM>
+template <int NM, int BS>
 __device__ __forceinline__ void tiles_mma_f16(f32x4 (&acc)[NM][kBT], const f16* const (&w)[NM], const int (&row)[kBT],
                                               int nt, const f16* __restrict__ x, int B, int K, int k_begin,
                                               int k_end) {
-  const int li = threadIdx.x & 15;
+  const int lane = threadIdx.x & (WAVE - 1), li = lane & 15, lk = lane >> 4;
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int t = 0; t < kBT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f16* xr = x + (size_t)li * K;
   const bool xok = li < B;
-  F16Step<NM> b0, b1;
-  f16_step_load(b0, w, row, nt, xr, xok, K, k_begin, k_end);
-  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
-    f16_step_load(b1, w, row, nt, xr, xok, K, k0 + 32, k_end);
-    f16_step_mma(acc, b0, nt);
-    if (k0 + 64 < k_end) f16_step_load(b0, w, row, nt, xr, xok, K, k0 + 64, k_end);
-    if (k0 + 32 < k_end) f16_step_mma(acc, b1, nt);
+  for (int k0 = k_begin; k0 < k_end; k0 += 32 * BS) {
+    // step st: lane (li, lk) reads 16 bytes of row li at element k0 + 32 * st + 8 * lk, so the
+    // batch covers 256 contiguous bytes of each row; X is read in the same order
+    u32x4 xa[BS], wv[BS][NM][kBT];
+#pragma unroll
+    for (int st = 0; st < BS; ++st) {
+      const int kk = k0 + 32 * st + 8 * lk;
+      const bool ok = k0 + 32 * st < k_end;
+      xa[st] = (xok && ok) ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int t = 0; t < kBT; ++t)
+#pragma unroll
+        for (int st = 0; st < BS; ++st) {
+          const int kk = k0 + 32 * st + 8 * lk;
+          const bool ok = k0 + 32 * st < k_end;
+          wv[st][m][t] = (ok && t < nt && row[t] >= 0)
+                             ? ld_stream(reinterpret_cast<const u32x4*>(w[m] + (size_t)row[t] * K + kk))
+                             : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+    for (int st = 0; st < BS; ++st)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < kBT; ++t)
+          if (t < nt) acc[m][t] = mma_f16(xa[st], wv[st][m][t], acc[m][t]);
   }
 }
 
@@ -143,36 +139,34 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
       f32x4 acc[kBT];
 #pragma unroll
       for (int q = 0; q < kBT; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-      struct P2Step {
-        u32x4 pw[kBT];
-        f32x4 hv[2];
-      };
-      auto load = [&](P2Step& st, int k0) {
-        const int kk = k0 + 8 * lk;
-        const bool ok = k0 < kb + kw;
+      for (int k0 = kb; k0 < kb + kw; k0 += 32 * kBS) {
+        u32x4 pw[kBS][kBT];
+        f32x4 hv[kBS][2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          st.hv[q] = (ok && li < B) ? *reinterpret_cast<const f32x4*>(hr + kk + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < kBS; ++st) {
+          const int kk = k0 + 32 * st + 8 * lk;
+          const bool ok = k0 + 32 * st < kb + kw;
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            hv[st][q] = (ok && li < B) ? *reinterpret_cast<const f32x4*>(hr + kk + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int q = 0; q < kBT; ++q) {
           const int row = g0 + 16 * q + li;
-          st.pw[q] = (ok && row < n) ? ld_stream(reinterpret_cast<const u32x4*>(p2 + (size_t)row * r + kk))
-                                     : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int st = 0; st < kBS; ++st) {
+            const int kk = k0 + 32 * st + 8 * lk;
+            const bool ok = k0 + 32 * st < kb + kw;
+            pw[st][q] = (ok && row < n) ? ld_stream(reinterpret_cast<const u32x4*>(p2 + (size_t)row * r + kk))
+                                        : u32x4{0, 0, 0, 0};
+          }
         }
-      };
-      auto mma = [&](const P2Step& st) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int st = 0; st < kBS; ++st)
 #pragma unroll
-          for (int q = 0; q < kBT; ++q) acc[q] = mma_f32(st.hv[e / 4][e % 4], half_at(st.pw[q], e), acc[q]);
-      };
-      P2Step st0, st1;
-      load(st0, kb);
-      for (int k0 = kb; k0 < kb + kw; k0 += 64) {
-        load(st1, k0 + 32);
-        mma(st0);
-        if (k0 + 64 < kb + kw) load(st0, k0 + 64);
-        if (k0 + 32 < kb + kw) mma(st1);
+          for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int q = 0; q < kBT; ++q) acc[q] = mma_f32(hv[st][e / 4][e % 4], half_at(pw[st][q], e), acc[q]);
       }
 #pragma unroll
       for (int q = 0; q < kBT; ++q) s_red[wave][0][q][lane] = acc[q];
@@ -186,7 +180,7 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
       const f16* const w[1] = {static_cast<const f16*>(A.gated ? A.w_gate : A.w_up)};
       f32x4 acc[1][kBT];
       const int kw = d / kBNW;
-      tiles_mma_f16<1>(acc, w, row, kBT, xb, B, d, wave * kw, (wave + 1) * kw);
+      tiles_mma_f16<1, kBS>(acc, w, row, kBT, xb, B, d, wave * kw, (wave + 1) * kw);
 #pragma unroll
       for (int q = 0; q < kBT; ++q) s_red[wave][0][q][lane] = acc[0][q];
       __syncthreads();
@@ -255,7 +249,7 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
     if (A.gated) {
       const f16* const w[1] = {static_cast<const f16*>(A.w_up)};
       f32x4 acc[1][kBT];
-      tiles_mma_f16<1>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+      tiles_mma_f16<1, kBS>(acc, w, row, nt, xb, B, d, kb, kb + kw);
 #pragma unroll
       for (int q = 0; q < kBT; ++q) s_red[wave][1][q][lane] = acc[0][q];
       __syncthreads();
@@ -264,7 +258,7 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
   } else if (A.gated) {
     const f16* const w[2] = {static_cast<const f16*>(A.w_gate), static_cast<const f16*>(A.w_up)};
     f32x4 acc[2][kBT];
-    tiles_mma_f16<2>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+    tiles_mma_f16<2, kBS>(acc, w, row, nt, xb, B, d, kb, kb + kw);
 #pragma unroll
     for (int q = 0; q < kBT; ++q) {
       s_red[wave][0][q][lane] = acc[0][q];
@@ -278,7 +272,7 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
   } else {
     const f16* const w[1] = {static_cast<const f16*>(A.w_up)};
     f32x4 acc[1][kBT];
-    tiles_mma_f16<1>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+    tiles_mma_f16<1, kBS>(acc, w, row, nt, xb, B, d, kb, kb + kw);
 #pragma unroll
     for (int q = 0; q < kBT; ++q) s_red[wave][1][q][lane] = acc[0][q];
     __syncthreads();
