@@ -28,6 +28,8 @@ PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "group": PI_PHASE_GROUP, "down": 
           "finish": PI_PHASE_FINISH}
 STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_ERR_HIP", 4: "PI_ERR_UNSUPPORTED"}
 
+ABI_VERSION = 3   # PI_FFN_ABI_VERSION of the header this binding follows
+
 EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",
             "pi_ffn_destroy", "pi_ffn_predict", "pi_ffn_forward", "pi_ffn_forward_masked",
             "pi_ffn_launch_plan", "pi_ffn_profile_next")
@@ -77,6 +79,9 @@ def _load() -> ctypes.CDLL:
     lib.pi_ffn_launch_plan.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_uint32)]
     lib.pi_ffn_profile_next.restype = st
     lib.pi_ffn_profile_next.argtypes = [vp, i32, vp, vp]
+    got = lib.pi_ffn_abi_version()
+    if got != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {got}, this binding expects {ABI_VERSION}; rebuild it")
     return lib
 
 
