@@ -84,7 +84,7 @@ Layout layout_for(const pi_ffn_desc& d) {
   // partials: one [B][d] block per group workgroup, or per down chunk on the batched path
   L.max_partials = L.n_groups;
   if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
-  L.max_partials = std::max(L.max_partials, pik::wave_grid(d.d_ffn));
+  L.max_partials = std::max(L.max_partials, pik::wave_grid(d.d_ffn, d.d_model));
   L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.max_partials * B * dm);
   L.total = off;
   return L;
@@ -236,7 +236,7 @@ Plan plan_for(const pi_ffn* h, int mode, int B) {
   const pi_ffn_desc& d = h->desc;
   Plan p{};
   p.batched = pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank);
-  p.wave = !p.batched && pik::wave_supported(d.w_dtype, d.act_dtype, d.p_dtype, mode, B, d.d_model);
+  p.wave = !p.batched && pik::wave_supported(d.w_dtype, d.act_dtype, d.p_dtype, mode, B, d.d_model, d.rank);
   return p;
 }
 
@@ -261,7 +261,7 @@ pi_status group_phase(pi_ffn* h, int mode, const Plan& plan, const pik::GroupArg
                      [&] { return pik::launch_ffn_bdown(mode, a, h->abuf(), chunks, s); });
   }
   if (plan.wave) {
-    *partials = pik::wave_grid(d.d_ffn);
+    *partials = pik::wave_grid(d.d_ffn, d.d_model);
     return run_phase(h, PI_PHASE_GROUP, s, "ffn_wave",
                      [&] { return pik::launch_ffn_wave(a, s); });
   }

@@ -1,5 +1,6 @@
 // The one-token predicted step with wave-independent neuron ownership (fp16 weights,
-// activations and predictor, d = 512 * CPLF up to 4096).
+// activations and predictor): k_ffn_wave for d = 512 * CPLF up to 4096, k_ffn_wave2 (wave
+// pairs, half a row each) for d = 1024 * CPLH from 5120 to 8192.
 //
 // A workgroup owns a byte-aligned range of about n / (#CUs) neurons, one workgroup per CU, and
 // splits it into 8 waves of at most kWRows consecutive neurons.  Each wave, on its own:
@@ -145,6 +146,198 @@ __global__ __launch_bounds__(kWWaves * WAVE) void k_ffn_wave(const GroupArgs A, 
     for (int w = 0; w < kWWaves; ++w) {
       if ((busy >> w) & 1u) {
         v = first ? s_y[w][k] : v + s_y[w][k];
+        first = false;
+      }
+    }
+    *reinterpret_cast<f32x4*>(dst + 4 * k) = v;
+  }
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// k_ffn_wave2: the same step for 4096 < d <= 8192 (d a multiple of 1024), where a whole row no
+// longer fits one wave's registers.  The 8 waves form 4 pairs; the two waves of a pair take
+// the two halves of d (and of r for the predictor).
+//   mask    each pair computes the half-r partial logits of a quarter of the workgroup's
+//           neurons; after a barrier one thread per neuron adds the halves (first + second)
+//           and the bias, and the decisions become a ballot bit set;
+//   gather  after a second barrier the selected neurons are dealt round-robin to the pairs
+//           in ascending order, so each pair handles at most ceil(selected / 4).  For each
+//           neuron both waves of the pair load their halves of the three rows, exchange their
+//           partial gate and up sums through LDS (each wave raises its own LDS step counter
+//           and waits for its partner's: both walk the same list, so they take the same steps,
+//           and the partner is a wave of the same workgroup that waits on nothing else), form
+//           the activation identically, and add a * W_down^T over their half of d.
+// At the end each pair's y halves are added in pair order through LDS, so the result is the
+// same on every run.
+// ---------------------------------------------------------------------------------------------
+constexpr int kW2Pairs = 4;                          // wave pairs per workgroup (8 waves)
+constexpr int kW2Rows = 32;                          // predictor rows per pair
+constexpr int kW2Max = kW2Pairs * kW2Rows;           // most neurons one workgroup owns (128)
+constexpr int kW2Units = kW2Max / 8;
+
+template <int CPLH>   // 16-byte chunks per lane of a half row (d = 1024 * CPLH)
+__global__ __launch_bounds__(2 * kW2Pairs * WAVE) void k_ffn_wave2(const GroupArgs A, int n_units) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int pair = wave >> 1, half = wave & 1;
+  const int n = A.n, d = A.d, r = A.r;
+  const int u0 = (int)((long long)blockIdx.x * n_units / gridDim.x);
+  const int u1 = (int)((long long)(blockIdx.x + 1) * n_units / gridDim.x);
+  const int r0 = 8 * u0, r1 = min(n, 8 * u1);        // r1 - r0 <= kW2Max
+  const int dh = d / 2, rh = r / 2;                  // this wave's halves of d and r
+
+  __shared__ unsigned s_bits[kW2Max / 32];
+  __shared__ unsigned s_busy;                        // bit p: pair p handled a neuron
+  __shared__ int s_step[2 * kW2Pairs];               // steps each wave has published
+  __shared__ float s_z[2][kW2Max];                   // partial logits by half of r
+  __shared__ float s_gu[kW2Pairs][2][2][2];          // [pair][step parity][half][g, u]
+  __shared__ f32x4 s_y[2 * kW2Pairs][CPLH * WAVE * 2];
+
+  if (threadIdx.x == 0) s_busy = 0u;
+  if ((int)threadIdx.x < 2 * kW2Pairs) s_step[threadIdx.x] = 0;
+
+  // ---- mask: a quarter of the workgroup's rows per pair, this wave's half of r -----------------
+  {
+    const f16* p2 = static_cast<const f16*>(A.p2);
+    const int rpp = (r1 - r0 + kW2Pairs - 1) / kW2Pairs;   // <= kW2Rows
+    const int q0 = r0 + pair * rpp, q1 = min(r1, q0 + rpp);
+    const bool cok = 8 * lane < rh;
+    u32x4 pw[kW2Rows];
+#pragma unroll
+    for (int j = 0; j < kW2Rows; ++j)
+      pw[j] = (q0 + j < q1 && cok)
+                  ? ld_stream(reinterpret_cast<const u32x4*>(p2 + (size_t)(q0 + j) * r + half * rh) + lane)
+                  : u32x4{0, 0, 0, 0};
+    XChunk<DT_F16, DT_F32> hx;
+    if (cok) hx.load(A.h + half * rh + 8 * lane);
+    else hx.zero();
+#pragma unroll
+    for (int j = 0; j < kW2Rows; ++j) {
+      float a = 0.f;
+      dot_chunk<DT_F16, DT_F32>(a, pw[j], hx, 1.f);
+      const float zp = wave_sum(a);
+      if (lane == 0 && q0 + j < q1) s_z[half][q0 - r0 + j] = zp;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kW2Max) {   // waves 0 and 1: one neuron per thread
+    const int t = threadIdx.x;
+    bool sel = false;
+    if (r0 + t < r1) {
+      const float v = (s_z[0][t] + s_z[1][t]) + A.b_p[r0 + t];
+      if (A.logits != nullptr) A.logits[r0 + t] = v;
+      sel = v > A.thr;
+    }
+    const unsigned long long bal = __ballot(sel);
+    if (lane == 0) {
+      s_bits[2 * wave] = (unsigned)bal;
+      s_bits[2 * wave + 1] = (unsigned)(bal >> 32);
+    }
+  }
+  __syncthreads();
+
+  // ---- gather: this pair's share of the selected neurons, this wave's half of every row --------
+  constexpr int NE = 8;
+  float acc[CPLH][NE];
+#pragma unroll
+  for (int q = 0; q < CPLH; ++q)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[q][e] = 0.f;
+  bool busy = false;
+  if (!A.mask_only) {
+    int step = 0;
+    const f16* xb = static_cast<const f16*>(A.x) + half * dh;
+    XChunk<DT_F16, DT_F16> xq[CPLH];
+    const size_t rbytes = row_bytes(DT_F16, d), hoff = row_bytes(DT_F16, dh) * half;
+    const char* wgb = static_cast<const char*>(A.w_gate) + hoff;
+    const char* wub = static_cast<const char*>(A.w_up) + hoff;
+    const char* wdb = static_cast<const char*>(A.w_down_t) + hoff;
+    int rank = 0;   // rank of the next selected neuron in the workgroup's ascending list
+#pragma unroll 1
+    for (int w = 0; w < kW2Max / 32; ++w) {
+      unsigned m = s_bits[w];
+      while (m != 0u) {
+        const int j = __ffs((int)m) - 1;
+        m &= m - 1u;
+        if ((rank++ & (kW2Pairs - 1)) != pair) continue;
+        if (!busy) {
+#pragma unroll
+          for (int q = 0; q < CPLH; ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * 8);
+          busy = true;
+        }
+        const int id = r0 + 32 * w + j;
+        const float bj = A.b[id];
+        u32x4 wg[CPLH], wu[CPLH], wd[CPLH];
+#pragma unroll
+        for (int q = 0; q < CPLH; ++q) {
+          const int c = lane + q * WAVE;
+          wg[q] = A.gated ? ld_stream(reinterpret_cast<const u32x4*>(wgb + rbytes * id) + c) : u32x4{0, 0, 0, 0};
+          wu[q] = ld_stream(reinterpret_cast<const u32x4*>(wub + rbytes * id) + c);
+          wd[q] = ld_stream(reinterpret_cast<const u32x4*>(wdb + rbytes * id) + c);
+        }
+        float pg = 0.f, pu = 0.f;
+#pragma unroll
+        for (int q = 0; q < CPLH; ++q) {
+          if (A.gated) dot_chunk<DT_F16, DT_F16>(pg, wg[q], xq[q], 1.f);
+          dot_chunk<DT_F16, DT_F16>(pu, wu[q], xq[q], 1.f);
+        }
+        const float gh = A.gated ? wave_sum(pg) : 0.f;
+        const float uh = wave_sum(pu);
+        const int slot = step & 1;
+        if (lane == 0) {
+          s_gu[pair][slot][half][0] = gh;
+          s_gu[pair][slot][half][1] = uh;
+        }
+        // publish this wave's step, then wait for the partner's: the two-slot ring is safe
+        // because a wave reuses a slot only after its partner has published the step after
+        // the one that read it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        ++step;
+        if (lane == 0) __hip_atomic_store(&s_step[wave], step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        while (__hip_atomic_load(&s_step[wave ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < step)
+          __builtin_amdgcn_s_sleep(1);
+        const float g = s_gu[pair][slot][0][0] + s_gu[pair][slot][1][0];
+        const float u = s_gu[pair][slot][0][1] + s_gu[pair][slot][1][1];
+        const float a = A.gated ? fmaxf(g + bj, 0.f) * u : fmaxf(u + bj, 0.f);
+#pragma unroll
+        for (int q = 0; q < CPLH; ++q) {
+          float wf[NE];
+          Unpack<DT_F16>::run(wd[q], wf);
+#pragma unroll
+          for (int e = 0; e < NE; ++e) acc[q][e] = fmaf(a, wf[e], acc[q][e]);
+        }
+      }
+    }
+  }
+
+  // ---- the workgroup's mask bytes and partial of y ---------------------------------------------
+  if ((int)threadIdx.x < u1 - u0) {
+    const int bo = 8 * (int)threadIdx.x;
+    reinterpret_cast<unsigned char*>(A.mask_words)[u0 + threadIdx.x] =
+        (unsigned char)(s_bits[bo / 32] >> (bo % 32));
+  }
+  if (A.mask_only) return;
+  if (busy) {
+#pragma unroll
+    for (int q = 0; q < CPLH; ++q) {
+      const int c = lane + q * WAVE;
+      s_y[wave][2 * c] = f32x4{acc[q][0], acc[q][1], acc[q][2], acc[q][3]};
+      s_y[wave][2 * c + 1] = f32x4{acc[q][4], acc[q][5], acc[q][6], acc[q][7]};
+    }
+    if (half == 0 && lane == 0) atomicOr(&s_busy, 1u << pair);
+  }
+  __syncthreads();
+  const unsigned bmask = s_busy;
+  float* dst = A.partial + (size_t)blockIdx.x * d;
+  constexpr int kQH = CPLH * WAVE * 2;   // float4 quads in half a row
+  for (int k = threadIdx.x; k < 2 * kQH; k += blockDim.x) {
+    const int hh = k / kQH, kk = k % kQH;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    bool first = true;
+#pragma unroll
+    for (int p = 0; p < kW2Pairs; ++p) {
+      if ((bmask >> p) & 1u) {
+        v = first ? s_y[2 * p + hh][kk] : v + s_y[2 * p + hh][kk];
         first = false;
       }
     }

@@ -5,20 +5,35 @@
 
 namespace pik {
 
-bool wave_supported(int wt, int at, int pt, int mode, int B, int d) {
-  return mode == MODE_PRED && B == 1 && wt == DT_F16 && at == DT_F16 && pt == DT_F16 && d % 512 == 0 && d >= 512 &&
-         d <= 4096;
+bool wave_supported(int wt, int at, int pt, int mode, int B, int d, int r) {
+  if (mode != MODE_PRED || B != 1 || wt != DT_F16 || at != DT_F16 || pt != DT_F16) return false;
+  if (d >= 512 && d <= 4096) return d % 512 == 0;
+  // wave pairs: each wave holds half a row of d and takes half of r in one 16-byte chunk per lane
+  return d > 4096 && d <= 8192 && d % 1024 == 0 && r % 16 == 0 && r <= 16 * WAVE;
 }
 
-int wave_grid(int n) {
+int wave_grid(int n, int d) {
   const int units = (n + 7) / 8;
-  const int need = (units + kWRows - 1) / kWRows;     // at most kWRows units (64 neurons) per workgroup
-  return std::min(units, std::max(kWaveGridBase, need));
+  // at most kWRows units (64 neurons) per one-wave workgroup, kW2Units (128) per wave-pair one
+  const int per = d > 4096 ? kW2Units : kWRows;
+  return std::min(units, std::max(kWaveGridBase, (units + per - 1) / per));
 }
 
 hipError_t launch_ffn_wave(const GroupArgs& a, hipStream_t s) {
   const int units = (a.n + 7) / 8;
-  const dim3 grid(wave_grid(a.n)), block(kWWaves * WAVE);
+  const dim3 grid(wave_grid(a.n, a.d));
+  if (a.d > 4096) {
+    const dim3 block(2 * kW2Pairs * WAVE);
+    switch (a.d / 1024) {
+#define PIK_WAVE2(C) \
+  case C: hipLaunchKernelGGL((k_ffn_wave2<C>), grid, block, 0, s, a, units); break;
+      PIK_WAVE2(5) PIK_WAVE2(6) PIK_WAVE2(7) PIK_WAVE2(8)
+#undef PIK_WAVE2
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const dim3 block(kWWaves * WAVE);
   switch (a.d / 512) {
 #define PIK_WAVE(C) \
   case C: hipLaunchKernelGGL((k_ffn_wave<C>), grid, block, 0, s, a, units); break;

@@ -1,6 +1,7 @@
-"""GPU parity of the wave-independent one-token predicted kernel (fp16 weights,
-activations and predictor, batch 1, d a multiple of 512 up to 4096) against the
-CPU oracle.
+"""GPU parity of the wave-independent one-token predicted kernels (fp16 weights,
+activations and predictor, batch 1) against the CPU oracle: one wave per neuron
+for d a multiple of 512 up to 4096, a wave pair per neuron (each wave half of d
+and of r) for d a multiple of 1024 from 5120 to 8192 with r <= 1024.
 
 Integer-lattice layers make every sum exact, so the index list, the logits and
 y must match the oracle bit for bit.  Shapes cover workgroups of one 8-neuron
@@ -58,6 +59,43 @@ def test_lattice_bit_exact_wave(d, n, r, gated):
         pidx, _, z = run_predict(h, x)
         assert np.array_equal(pidx, ref["idx"])
         assert np.array_equal(z.astype(np.float64), ref["z"])
+    h.close()
+
+
+@pytest.mark.parametrize("d,n,r,gated", [
+    (5120, 1000, 128, True),     # one unit per workgroup: pairs of 2 neurons, two pairs idle
+    (6144, 11000, 512, False),   # 5-6 units per workgroup
+    (7168, 3000, 1024, False),   # the OPT-30B width and predictor rank
+    (8192, 20000, 256, True),    # 9-10 units per workgroup: 18-20 neurons per pair, mask bits across words
+    (5120, 40000, 128, False),   # 15-16 units per workgroup: up to 32 neurons per pair
+    (5120, 1000, 2048, True),    # r above 1024: the vector path
+])
+def test_lattice_bit_exact_wave_pairs(d, n, r, gated):
+    announce(f"wave-pair kernel lattice d={d} n={n} r={r} gated={gated}")
+    layer = make_lattice_layer(d, n, r, gated, seed=d + n + r)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    for t in range(2):
+        x = make_lattice_tokens(d, 1, seed=60 + t)
+        ref = oracle.forward(layer, x, "predicted")
+        idx, count, y = run_forward(h, x, "predicted")
+        check_idx_valid(idx, count, n)
+        assert count == ref["count"] and np.array_equal(idx, ref["idx"]), f"token {t}"
+        assert _bitwise(y, ref["y"]), f"token {t}: y differs bitwise"
+        pidx, _, z = run_predict(h, x)
+        assert np.array_equal(pidx, ref["idx"])
+        assert np.array_equal(z.astype(np.float64), ref["z"])
+    h.close()
+
+
+def test_lattice_wave_pairs_nothing_selected():
+    d, n, r = 8192, 3000, 256
+    announce("wave-pair kernel: no neuron selected")
+    layer = make_lattice_layer(d, n, r, False, seed=79)
+    layer.b_p = np.full(n, -1000.0, dtype=np.float32)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    idx, count, y = run_forward(h, make_lattice_tokens(d, 1, seed=80), "predicted")
+    assert count == 0
+    assert np.all(y == 0) and not np.signbit(y).any()
     h.close()
 
 
