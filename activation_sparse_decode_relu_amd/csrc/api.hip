@@ -84,7 +84,7 @@ Layout layout_for(const pi_ffn_desc& d) {
   // partials: one [B][d] block per group workgroup, or per down chunk on the batched path
   L.max_partials = L.n_groups;
   if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
-  L.max_partials = std::max(L.max_partials, pik::wave_grid(d.d_ffn, d.d_model));
+  L.max_partials = std::max(L.max_partials, pik::wave_grid(d.d_ffn, d.d_model, d.w_dtype));
   L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.max_partials * B * dm);
   L.total = off;
   return L;
@@ -261,9 +261,9 @@ pi_status group_phase(pi_ffn* h, int mode, const Plan& plan, const pik::GroupArg
                      [&] { return pik::launch_ffn_bdown(mode, a, h->abuf(), chunks, s); });
   }
   if (plan.wave) {
-    *partials = pik::wave_grid(d.d_ffn, d.d_model);
+    *partials = pik::wave_grid(d.d_ffn, d.d_model, d.w_dtype);
     return run_phase(h, PI_PHASE_GROUP, s, "ffn_wave",
-                     [&] { return pik::launch_ffn_wave(a, s); });
+                     [&] { return pik::launch_ffn_wave(d.w_dtype, a, s); });
   }
   *partials = h->L.n_groups;
   return run_phase(h, PI_PHASE_GROUP, s, "ffn_group",

@@ -51,13 +51,15 @@ int batch_down_chunks(int d);
 hipError_t launch_ffn_bgroup(int mode, const GroupArgs& a, float* abuf, hipStream_t s);
 hipError_t launch_ffn_bdown(int mode, const GroupArgs& a, const float* abuf, int chunks, hipStream_t s);
 
-// The wave-independent one-token predicted kernel (fp16; d = 512 .. 4096 in steps of 512, or
-// 5120 .. 8192 in steps of 1024 with r <= 1024 on wave pairs), each
-// writing one partial of y and whole bytes of the mask; wave_grid(n, d) workgroups.
+// The wave-independent one-token predicted kernels (fp16 activations and predictor; fp16
+// weights with d = 512 .. 4096 in steps of 512 on single waves, or d = 5120 .. 8192 in steps of
+// 1024 on wave pairs; int4 weights with d = 4096 or 8192 on wave pairs; wave pairs need
+// r <= 1024): wave_grid(n, d, wt) workgroups, each writing one partial of y and whole bytes of
+// the mask.
 constexpr int kWaveGridBase = 256;   // one workgroup per compute unit of an MI355X
 bool wave_supported(int wt, int at, int pt, int mode, int B, int d, int r);
-int wave_grid(int n, int d);   // at most wave_grid(n, 512) for any d
-hipError_t launch_ffn_wave(const GroupArgs& a, hipStream_t s);
+int wave_grid(int n, int d, int wt);   // at most (n + 7) / 8, and at most wave_grid(n, 512, fp16)
+hipError_t launch_ffn_wave(int wt, const GroupArgs& a, hipStream_t s);
 
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
                          const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,

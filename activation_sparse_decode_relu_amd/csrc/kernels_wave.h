@@ -1,6 +1,6 @@
 // The one-token predicted step with wave-independent neuron ownership (fp16 weights,
-// activations and predictor): k_ffn_wave for d = 512 * CPLF up to 4096, k_ffn_wave2 (wave
-// pairs, half a row each) for d = 1024 * CPLH from 5120 to 8192.
+// activations and predictor): k_ffn_wave for fp16 rows with d = 512 * CPLF up to 4096,
+// k_ffn_wave2 (wave pairs, half a row each) for fp16 with d from 5120 to 8192 and int4.
 //
 // A workgroup owns a byte-aligned range of about n / (#CUs) neurons, one workgroup per CU, and
 // splits it into 8 waves of at most kWRows consecutive neurons.  Each wave, on its own:
@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kWWaves * WAVE) void k_ffn_wave(const GroupArgs A, 
 
   __shared__ unsigned s_bits[2];                    // the workgroup's decisions (at most 64 neurons)
   __shared__ unsigned s_busy;                       // bit w: wave w selected a neuron and stored its y
-  __shared__ f32x4 s_y[kWWaves][CPLF * WAVE * 2];   // each wave's y, 8 floats per 16-byte chunk
+  constexpr int kCF = CPLF * WAVE;                  // 16-byte chunks in a row
+  __shared__ f32x4 s_y[kWWaves][2 * (kCF + 1)];     // each wave's y: quad k of chunk c at k * (kCF + 1) + c
 
   if (threadIdx.x < 2) s_bits[threadIdx.x] = 0u;
   if (threadIdx.x == 0) s_busy = 0u;
@@ -125,8 +126,8 @@ __global__ __launch_bounds__(kWWaves * WAVE) void k_ffn_wave(const GroupArgs A, 
 #pragma unroll
     for (int q = 0; q < CPLF; ++q) {
       const int c = lane + q * WAVE;
-      s_y[wave][2 * c] = f32x4{acc[q][0], acc[q][1], acc[q][2], acc[q][3]};
-      s_y[wave][2 * c + 1] = f32x4{acc[q][4], acc[q][5], acc[q][6], acc[q][7]};
+      s_y[wave][c] = f32x4{acc[q][0], acc[q][1], acc[q][2], acc[q][3]};
+      s_y[wave][kCF + 1 + c] = f32x4{acc[q][4], acc[q][5], acc[q][6], acc[q][7]};
     }
     if (lane == 0) atomicOr(&s_busy, 1u << wave);
   }
@@ -139,13 +140,14 @@ __global__ __launch_bounds__(kWWaves * WAVE) void k_ffn_wave(const GroupArgs A, 
   if (A.mask_only) return;
   const unsigned busy = s_busy;
   float* dst = A.partial + (size_t)blockIdx.x * d;
-  for (int k = threadIdx.x; k < CPLF * WAVE * 2; k += blockDim.x) {
+  for (int k = threadIdx.x; k < 2 * kCF; k += blockDim.x) {   // quad k of the row
+    const int slot = (k & 1) * (kCF + 1) + (k >> 1);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     bool first = true;
 #pragma unroll
     for (int w = 0; w < kWWaves; ++w) {
       if ((busy >> w) & 1u) {
-        v = first ? s_y[w][k] : v + s_y[w][k];
+        v = first ? s_y[w][slot] : v + s_y[w][slot];
         first = false;
       }
     }
@@ -155,29 +157,34 @@ __global__ __launch_bounds__(kWWaves * WAVE) void k_ffn_wave(const GroupArgs A, 
 
 
 // ---------------------------------------------------------------------------------------------
-// k_ffn_wave2: the same step for 4096 < d <= 8192 (d a multiple of 1024), where a whole row no
-// longer fits one wave's registers.  The 8 waves form 4 pairs; the two waves of a pair take
-// the two halves of d (and of r for the predictor).
+// k_ffn_wave2: the same step on wave pairs, for layers whose rows do not fit one wave's
+// registers: fp16 with d = 1024 * CPLH (5120 .. 8192), and int4 group-32 with d = 4096 * CPLH.
+// The 8 waves form 4 pairs; the two waves of a pair take the two halves of d (and of r for the
+// predictor).
 //   mask    each pair computes the half-r partial logits of a quarter of the workgroup's
 //           neurons; after a barrier one thread per neuron adds the halves (first + second)
-//           and the bias, and the decisions become a ballot bit set;
-//   gather  after a second barrier the selected neurons are dealt round-robin to the pairs
-//           in ascending order, so each pair handles at most ceil(selected / 4).  For each
-//           neuron both waves of the pair load their halves of the three rows, exchange their
-//           partial gate and up sums through LDS (each wave raises its own LDS step counter
-//           and waits for its partner's: both walk the same list, so they take the same steps,
+//           and the bias, and the decisions become a ballot bit set and then the workgroup's
+//           ascending list of selected neurons;
+//   gather  the list is dealt round-robin to the pairs (pair p takes entries p, p + 4, ...), so
+//           each pair handles at most ceil(selected / 4), NJ neurons per step.  For each step
+//           both waves of the pair load their halves of the NJ neurons' rows, exchange their
+//           partial gate and up sums through LDS (each wave raises its own LDS step counter and
+//           waits for its partner's: both walk the same entries, so they take the same steps,
 //           and the partner is a wave of the same workgroup that waits on nothing else), form
-//           the activation identically, and add a * W_down^T over their half of d.
+//           the activations identically, and add a * W_down^T over their half of d.
 // At the end each pair's y halves are added in pair order through LDS, so the result is the
-// same on every run.
+// same on every run.  int4 rows are one group of 32 per 16-byte chunk: a chunk's scale
+// multiplies its partial gate / up sum, and multiplies a for its slice of the down row.
 // ---------------------------------------------------------------------------------------------
 constexpr int kW2Pairs = 4;                          // wave pairs per workgroup (8 waves)
 constexpr int kW2Rows = 32;                          // predictor rows per pair
 constexpr int kW2Max = kW2Pairs * kW2Rows;           // most neurons one workgroup owns (128)
 constexpr int kW2Units = kW2Max / 8;
 
-template <int CPLH>   // 16-byte chunks per lane of a half row (d = 1024 * CPLH)
+template <int WT, int CPLH, int NJ>   // chunks per lane of a half row; neurons per exchange step
 __global__ __launch_bounds__(2 * kW2Pairs * WAVE) void k_ffn_wave2(const GroupArgs A, int n_units) {
+  constexpr int EPC = WFmt<WT>::EPC;                 // elements per 16-byte chunk
+  constexpr int kQH = CPLH * WAVE * EPC / 4;         // float4 quads in half a row
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int pair = wave >> 1, half = wave & 1;
   const int n = A.n, d = A.d, r = A.r;
@@ -187,11 +194,13 @@ __global__ __launch_bounds__(2 * kW2Pairs * WAVE) void k_ffn_wave2(const GroupAr
   const int dh = d / 2, rh = r / 2;                  // this wave's halves of d and r
 
   __shared__ unsigned s_bits[kW2Max / 32];
+  __shared__ int s_list[kW2Max];                     // the selected neurons, ascending
   __shared__ unsigned s_busy;                        // bit p: pair p handled a neuron
   __shared__ int s_step[2 * kW2Pairs];               // steps each wave has published
   __shared__ float s_z[2][kW2Max];                   // partial logits by half of r
-  __shared__ float s_gu[kW2Pairs][2][2][2];          // [pair][step parity][half][g, u]
-  __shared__ f32x4 s_y[2 * kW2Pairs][CPLH * WAVE * 2];
+  __shared__ float s_gu[kW2Pairs][2][2][NJ][2];      // [pair][step parity][half][neuron][g, u]
+  constexpr int kCH = CPLH * WAVE;                  // chunks in half a row
+  __shared__ f32x4 s_y[2 * kW2Pairs][(EPC / 4) * (kCH + 1)];
 
   if (threadIdx.x == 0) s_busy = 0u;
   if ((int)threadIdx.x < 2 * kW2Pairs) s_step[threadIdx.x] = 0;
@@ -235,76 +244,118 @@ __global__ __launch_bounds__(2 * kW2Pairs * WAVE) void k_ffn_wave2(const GroupAr
     }
   }
   __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kW2Max / 32; ++w) total += __popc(s_bits[w]);
+  if (threadIdx.x < kW2Max) {
+    const int t = threadIdx.x, w = t / 32, b = t % 32;
+    if ((s_bits[w] >> b) & 1u) {
+      int pos = __popc(s_bits[w] & ((1u << b) - 1u));
+      for (int k = 0; k < w; ++k) pos += __popc(s_bits[k]);
+      s_list[pos] = r0 + t;
+    }
+  }
+  __syncthreads();
 
-  // ---- gather: this pair's share of the selected neurons, this wave's half of every row --------
-  constexpr int NE = 8;
-  float acc[CPLH][NE];
+  // ---- gather: list entries pair, pair + 4, ...; this wave's half of every row ----------------
+  float acc[CPLH][EPC];
 #pragma unroll
   for (int q = 0; q < CPLH; ++q)
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[q][e] = 0.f;
-  bool busy = false;
-  if (!A.mask_only) {
+    for (int e = 0; e < EPC; ++e) acc[q][e] = 0.f;
+  const int share = (total - pair + kW2Pairs - 1) / kW2Pairs;   // entries this pair handles
+  const bool busy = !A.mask_only && share > 0;
+  if (busy) {
     int step = 0;
     const f16* xb = static_cast<const f16*>(A.x) + half * dh;
-    XChunk<DT_F16, DT_F16> xq[CPLH];
-    const size_t rbytes = row_bytes(DT_F16, d), hoff = row_bytes(DT_F16, dh) * half;
+    XChunk<WT, DT_F16> xq[CPLH];
+#pragma unroll
+    for (int q = 0; q < CPLH; ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * EPC);
+    const size_t rbytes = row_bytes(WT, d), hoff = row_bytes(WT, dh) * half;
+    const int spr = d / 32, soff = half * (dh / 32);   // int4 scales per row, this half's first
     const char* wgb = static_cast<const char*>(A.w_gate) + hoff;
     const char* wub = static_cast<const char*>(A.w_up) + hoff;
     const char* wdb = static_cast<const char*>(A.w_down_t) + hoff;
-    int rank = 0;   // rank of the next selected neuron in the workgroup's ascending list
 #pragma unroll 1
-    for (int w = 0; w < kW2Max / 32; ++w) {
-      unsigned m = s_bits[w];
-      while (m != 0u) {
-        const int j = __ffs((int)m) - 1;
-        m &= m - 1u;
-        if ((rank++ & (kW2Pairs - 1)) != pair) continue;
-        if (!busy) {
+    for (int k0 = 0; k0 < share; k0 += NJ) {
+      int id[NJ];
+      bool ok[NJ];
 #pragma unroll
-          for (int q = 0; q < CPLH; ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * 8);
-          busy = true;
-        }
-        const int id = r0 + 32 * w + j;
-        const float bj = A.b[id];
-        u32x4 wg[CPLH], wu[CPLH], wd[CPLH];
+      for (int jj = 0; jj < NJ; ++jj) {
+        ok[jj] = k0 + jj < share;
+        id[jj] = ok[jj] ? s_list[pair + kW2Pairs * (k0 + jj)] : 0;
+      }
+      // Every load of the step is issued before any is used: rows, biases and (int4) the raw
+      // scales, the latter two from a valid neuron (id 0) for empty entries and dropped after.
+      u32x4 wg[NJ][CPLH], wu[NJ][CPLH], wd[NJ][CPLH];
+      f16 rsg[NJ][CPLH], rsu[NJ][CPLH], rsd[NJ][CPLH];
+      float bj[NJ];
+      const f16* sgp = A.gated ? A.s_gate : A.s_up;
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        bj[jj] = A.b[id[jj]];
 #pragma unroll
         for (int q = 0; q < CPLH; ++q) {
           const int c = lane + q * WAVE;
-          wg[q] = A.gated ? ld_stream(reinterpret_cast<const u32x4*>(wgb + rbytes * id) + c) : u32x4{0, 0, 0, 0};
-          wu[q] = ld_stream(reinterpret_cast<const u32x4*>(wub + rbytes * id) + c);
-          wd[q] = ld_stream(reinterpret_cast<const u32x4*>(wdb + rbytes * id) + c);
+          const size_t off = rbytes * id[jj];
+          const bool g_ok = ok[jj] && A.gated;
+          wg[jj][q] = g_ok ? ld_stream(reinterpret_cast<const u32x4*>(wgb + off) + c) : u32x4{0, 0, 0, 0};
+          wu[jj][q] = ok[jj] ? ld_stream(reinterpret_cast<const u32x4*>(wub + off) + c) : u32x4{0, 0, 0, 0};
+          wd[jj][q] = ok[jj] ? ld_stream(reinterpret_cast<const u32x4*>(wdb + off) + c) : u32x4{0, 0, 0, 0};
+          if constexpr (WT == DT_Q4) {
+            const size_t so = (size_t)id[jj] * spr + soff + c;
+            rsg[jj][q] = sgp[so];
+            rsu[jj][q] = A.s_up[so];
+            rsd[jj][q] = A.s_down[so];
+          }
         }
+      }
+      float sg[NJ][CPLH], su[NJ][CPLH], sd[NJ][CPLH];
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int q = 0; q < CPLH; ++q) {
+          sg[jj][q] = (WT == DT_Q4 && ok[jj] && A.gated) ? (float)rsg[jj][q] : 1.f;
+          su[jj][q] = (WT == DT_Q4 && ok[jj]) ? (float)rsu[jj][q] : 1.f;
+          sd[jj][q] = (WT == DT_Q4 && ok[jj]) ? (float)rsd[jj][q] : 1.f;
+        }
+      const int slot = step & 1;
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
         float pg = 0.f, pu = 0.f;
 #pragma unroll
         for (int q = 0; q < CPLH; ++q) {
-          if (A.gated) dot_chunk<DT_F16, DT_F16>(pg, wg[q], xq[q], 1.f);
-          dot_chunk<DT_F16, DT_F16>(pu, wu[q], xq[q], 1.f);
+          if (A.gated) dot_chunk<WT, DT_F16>(pg, wg[jj][q], xq[q], sg[jj][q]);
+          dot_chunk<WT, DT_F16>(pu, wu[jj][q], xq[q], su[jj][q]);
         }
         const float gh = A.gated ? wave_sum(pg) : 0.f;
         const float uh = wave_sum(pu);
-        const int slot = step & 1;
         if (lane == 0) {
-          s_gu[pair][slot][half][0] = gh;
-          s_gu[pair][slot][half][1] = uh;
+          s_gu[pair][slot][half][jj][0] = gh;
+          s_gu[pair][slot][half][jj][1] = uh;
         }
-        // publish this wave's step, then wait for the partner's: the two-slot ring is safe
-        // because a wave reuses a slot only after its partner has published the step after
-        // the one that read it
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        ++step;
-        if (lane == 0) __hip_atomic_store(&s_step[wave], step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        while (__hip_atomic_load(&s_step[wave ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < step)
-          __builtin_amdgcn_s_sleep(1);
-        const float g = s_gu[pair][slot][0][0] + s_gu[pair][slot][1][0];
-        const float u = s_gu[pair][slot][0][1] + s_gu[pair][slot][1][1];
-        const float a = A.gated ? fmaxf(g + bj, 0.f) * u : fmaxf(u + bj, 0.f);
+      }
+      // publish this wave's step, then wait for the partner's: the two-slot ring is safe
+      // because a wave reuses a slot only after its partner has published the step after
+      // the one that read it
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      ++step;
+      if (lane == 0) __hip_atomic_store(&s_step[wave], step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      while (__hip_atomic_load(&s_step[wave ^ 1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < step)
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        if (!ok[jj]) continue;
+        const float g = s_gu[pair][slot][0][jj][0] + s_gu[pair][slot][1][jj][0];
+        const float u = s_gu[pair][slot][0][jj][1] + s_gu[pair][slot][1][jj][1];
+        const float a = A.gated ? fmaxf(g + bj[jj], 0.f) * u : fmaxf(u + bj[jj], 0.f);
 #pragma unroll
         for (int q = 0; q < CPLH; ++q) {
-          float wf[NE];
-          Unpack<DT_F16>::run(wd[q], wf);
+          float wf[EPC];
+          Unpack<WT>::run(wd[jj][q], wf);
+          const float as = a * sd[jj][q];
 #pragma unroll
-          for (int e = 0; e < NE; ++e) acc[q][e] = fmaf(a, wf[e], acc[q][e]);
+          for (int e = 0; e < EPC; ++e) acc[q][e] = fmaf(as, wf[e], acc[q][e]);
         }
       }
     }
@@ -317,31 +368,35 @@ __global__ __launch_bounds__(2 * kW2Pairs * WAVE) void k_ffn_wave2(const GroupAr
         (unsigned char)(s_bits[bo / 32] >> (bo % 32));
   }
   if (A.mask_only) return;
+  // y halves in LDS: quad k (elements 4k .. 4k+3) of chunk c at k * (kCH + 1) + c, so the lanes
+  // of a store touch consecutive 16-byte slots, and threads reading consecutive quads of a row
+  // below land on different banks
   if (busy) {
 #pragma unroll
     for (int q = 0; q < CPLH; ++q) {
       const int c = lane + q * WAVE;
-      s_y[wave][2 * c] = f32x4{acc[q][0], acc[q][1], acc[q][2], acc[q][3]};
-      s_y[wave][2 * c + 1] = f32x4{acc[q][4], acc[q][5], acc[q][6], acc[q][7]};
+#pragma unroll
+      for (int k = 0; k < EPC / 4; ++k)
+        s_y[wave][k * (kCH + 1) + c] = f32x4{acc[q][4 * k], acc[q][4 * k + 1], acc[q][4 * k + 2], acc[q][4 * k + 3]};
     }
     if (half == 0 && lane == 0) atomicOr(&s_busy, 1u << pair);
   }
   __syncthreads();
   const unsigned bmask = s_busy;
   float* dst = A.partial + (size_t)blockIdx.x * d;
-  constexpr int kQH = CPLH * WAVE * 2;   // float4 quads in half a row
-  for (int k = threadIdx.x; k < 2 * kQH; k += blockDim.x) {
-    const int hh = k / kQH, kk = k % kQH;
+  for (int g = threadIdx.x; g < 2 * kQH; g += blockDim.x) {   // quad g of the row
+    const int hh = g / kQH, gq = g % kQH;                      // half, quad within it
+    const int slot = (gq % (EPC / 4)) * (kCH + 1) + gq / (EPC / 4);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     bool first = true;
 #pragma unroll
     for (int p = 0; p < kW2Pairs; ++p) {
       if ((bmask >> p) & 1u) {
-        v = first ? s_y[2 * p + hh][kk] : v + s_y[2 * p + hh][kk];
+        v = first ? s_y[2 * p + hh][slot] : v + s_y[2 * p + hh][slot];
         first = false;
       }
     }
-    *reinterpret_cast<f32x4*>(dst + 4 * k) = v;
+    *reinterpret_cast<f32x4*>(dst + 4 * g) = v;
   }
 }
 

@@ -1,7 +1,8 @@
-"""GPU parity of the wave-independent one-token predicted kernels (fp16 weights,
+"""GPU parity of the wave-independent one-token predicted kernels (fp16
 activations and predictor, batch 1) against the CPU oracle: one wave per neuron
-for d a multiple of 512 up to 4096, a wave pair per neuron (each wave half of d
-and of r) for d a multiple of 1024 from 5120 to 8192 with r <= 1024.
+for fp16 rows with d a multiple of 512 up to 4096; a wave pair per neuron (each
+wave half of d and of r, r <= 1024) for fp16 rows with d a multiple of 1024 from
+5120 to 8192 and for int4 group-32 rows with d = 4096 or 8192.
 
 Integer-lattice layers make every sum exact, so the index list, the logits and
 y must match the oracle bit for bit.  Shapes cover workgroups of one 8-neuron
@@ -76,6 +77,29 @@ def test_lattice_bit_exact_wave_pairs(d, n, r, gated):
     h = _pi().upload_layer(layer, "cuda", max_batch=1)
     for t in range(2):
         x = make_lattice_tokens(d, 1, seed=60 + t)
+        ref = oracle.forward(layer, x, "predicted")
+        idx, count, y = run_forward(h, x, "predicted")
+        check_idx_valid(idx, count, n)
+        assert count == ref["count"] and np.array_equal(idx, ref["idx"]), f"token {t}"
+        assert _bitwise(y, ref["y"]), f"token {t}: y differs bitwise"
+        pidx, _, z = run_predict(h, x)
+        assert np.array_equal(pidx, ref["idx"])
+        assert np.array_equal(z.astype(np.float64), ref["z"])
+    h.close()
+
+
+@pytest.mark.parametrize("d,n,r,gated", [
+    (4096, 3000, 128, True),     # gated int4, one chunk per lane of each half row
+    (8192, 5000, 256, False),    # the Falcon-40B width, 2-3 units per workgroup
+    (8192, 33000, 1024, False),  # 16 units per workgroup: 32 neurons per pair, several steps per pair
+])
+def test_lattice_bit_exact_wave_pairs_int4(d, n, r, gated):
+    announce(f"wave-pair kernel int4 lattice d={d} n={n} r={r} gated={gated}")
+    layer = make_lattice_layer(d, n, r, gated, w_dtype="q4g32", seed=d + n + r + 1)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    assert h.launch_plan(1, "predicted") == ("pred_hidden", "group", "finish")
+    for t in range(2):
+        x = make_lattice_tokens(d, 1, seed=70 + t)
         ref = oracle.forward(layer, x, "predicted")
         idx, count, y = run_forward(h, x, "predicted")
         check_idx_valid(idx, count, n)
