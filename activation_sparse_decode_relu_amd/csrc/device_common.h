@@ -35,6 +35,9 @@ __host__ __device__ constexpr size_t row_bytes(int wt, size_t k) {
 // Weight rows are read exactly once per step: stream them past the caches.
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ u32x2 ld_stream(const u32x2* p) { return __builtin_nontemporal_load(p); }
+// Plain (cache-allocating) loads, for the batched kernel's 256-byte operand runs: neighbouring
+// runs of a row share cache lines.
+__device__ __forceinline__ u32x4 ld_cached(const u32x4* p) { return *p; }
 
 __device__ __forceinline__ f16x2 as_h2(unsigned v) { return __builtin_bit_cast(f16x2, v); }
 

@@ -91,7 +91,7 @@ __device__ __forceinline__ void tiles_mma_f16(f32x4 (&acc)[NM][kBT], const f16* 
           const int kk = k0 + 32 * st + 8 * lk;
           const bool ok = k0 + 32 * st < k_end;
           wv[st][m][t] = (ok && t < nt && row[t] >= 0)
-                             ? ld_stream(reinterpret_cast<const u32x4*>(w[m] + (size_t)row[t] * K + kk))
+                             ? ld_cached(reinterpret_cast<const u32x4*>(w[m] + (size_t)row[t] * K + kk))
                              : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
           for (int st = 0; st < kBS; ++st) {
             const int kk = k0 + 32 * st + 8 * lk;
             const bool ok = k0 + 32 * st < kb + kw;
-            pw[st][q] = (ok && row < n) ? ld_stream(reinterpret_cast<const u32x4*>(p2 + (size_t)row * r + kk))
+            pw[st][q] = (ok && row < n) ? ld_cached(reinterpret_cast<const u32x4*>(p2 + (size_t)row * r + kk))
                                         : u32x4{0, 0, 0, 0};
           }
         }

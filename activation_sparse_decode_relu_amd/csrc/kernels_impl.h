@@ -87,45 +87,56 @@ __global__ inline void k_fill_u32(unsigned* p, int n, unsigned v) {
 }
 
 // ---------------------------------------------------------------------------
-// a1: h[t][j] = max(sum_k x[t][k] P1[j][k], 0).  One wave per row of P1.
+// a1: h[t][j] = max(sum_k x[t][k] P1[j][k], 0).  One wave per row of P1; each
+// chunk of the row is loaded once and applied to every token of the batch
+// (tokens in blocks of 4, NB = the most tokens).
 // ---------------------------------------------------------------------------
 template <int PT, int AT, int NB, int U>
 __global__ __launch_bounds__(256) void k_pred_hidden(const void* __restrict__ p1, const void* __restrict__ x,
                                                      int d, int r, int B, float* __restrict__ h) {
   using XT = typename VecT<AT>::T;
   constexpr int EPC = WFmt<PT>::EPC;
+  constexpr int TB = NB < 4 ? NB : 4;             // tokens per block
   const int lane = threadIdx.x & (WAVE - 1);
+
   const int row = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-  if (row >= r) return;
-  const int nch = d / EPC;
-  const u32x4* wrow = reinterpret_cast<const u32x4*>(static_cast<const char*>(p1) + row_bytes(PT, (size_t)row * d));
-  const XT* xb = static_cast<const XT*>(x);
-  for (int t0 = 0; t0 < B; t0 += NB) {
+  if (row < r) {
+    const int nch = d / EPC;
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(static_cast<const char*>(p1) + row_bytes(PT, (size_t)row * d));
+    const XT* xb = static_cast<const XT*>(x);
     float acc[NB];
 #pragma unroll
     for (int t = 0; t < NB; ++t) acc[t] = 0.f;
     for (int c0 = 0; c0 < nch; c0 += WAVE * U) {
       u32x4 w[U];
-      XChunk<PT, AT> xv[U][NB];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * WAVE + lane;
         w[u] = c < nch ? ld_stream(wrow + c) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-          if (c < nch && t0 + t < B) xv[u][t].load(xb + (size_t)(t0 + t) * d + (size_t)c * EPC);
-          else xv[u][t].zero();
-        }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int t0 = 0; t0 < NB; t0 += TB) {
+        if (t0 >= B) break;
+        XChunk<PT, AT> xv[U][TB];
 #pragma unroll
-        for (int t = 0; t < NB; ++t) dot_chunk<PT, AT>(acc[t], w[u], xv[u][t], 1.f);
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * WAVE + lane;
+#pragma unroll
+          for (int t = 0; t < TB; ++t) {
+            if (c < nch && t0 + t < B) xv[u][t].load(xb + (size_t)(t0 + t) * d + (size_t)c * EPC);
+            else xv[u][t].zero();
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int t = 0; t < TB; ++t) dot_chunk<PT, AT>(acc[t0 + t], w[u], xv[u][t], 1.f);
+      }
     }
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
       const float s = wave_sum(acc[t]);
-      if (lane == 0 && t0 + t < B) h[(size_t)(t0 + t) * r + row] = fmaxf(s, 0.f);
+      if (lane == 0 && t < B) h[(size_t)t * r + row] = fmaxf(s, 0.f);
     }
   }
 }

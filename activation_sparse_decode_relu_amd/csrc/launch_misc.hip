@@ -23,10 +23,12 @@ hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t s) {
 
 hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int d, int r, int B, float* h,
                               hipStream_t s) {
+  if (B < 1 || B > kMaxTokens) return hipErrorInvalidValue;
   const dim3 grid((r + 3) / 4), block(kBlock);
-  return with_nb(B, [&](auto nbc) -> hipError_t {
+  // up to 4 tokens: 8 chunks per lane in flight; up to 16: 4 chunks (x registers for 16 tokens)
+  auto go = [&](auto nbc) -> hipError_t {
     constexpr int NB = decltype(nbc)::value;
-    constexpr int U = 8;
+    constexpr int U = NB <= 4 ? 8 : 4;
     if (pt == DT_F16 && at == DT_F16)
       hipLaunchKernelGGL((k_pred_hidden<DT_F16, DT_F16, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
     else if (pt == DT_F16 && at == DT_F32)
@@ -38,7 +40,10 @@ hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int
     else
       return hipErrorInvalidValue;
     return hipGetLastError();
-  });
+  };
+  if (B == 1) return go(std::integral_constant<int, 1>{});
+  if (B <= 4) return go(std::integral_constant<int, 4>{});
+  return go(std::integral_constant<int, 16>{});
 }
 
 hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s) {

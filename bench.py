@@ -248,6 +248,8 @@ def main() -> int:
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--tokens", type=int, default=64, help="distinct token inputs per layer, replayed round-robin")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's own)")
+    ap.add_argument("--rank", type=int, default=0,
+                    help="override the predictor rank r (0 = the workload's own); for rank sweeps")
     ap.add_argument("--profile-tokens", type=int, default=4, help="tokens of the per-kernel event pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -286,6 +288,10 @@ def main() -> int:
     from synth import config_by_name, make_layer, make_tokens
 
     cfg = config_by_name(args.config)
+    if args.rank:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, rank=args.rank,
+                                  workload=cfg.workload.replace(f"r={cfg.rank}", f"r={args.rank}"))
     B, mode = args.batch, args.mode
     if B not in cfg.batches and not (cfg.name == "toy" and B <= 16):
         print(f"note: batch {B} is not one of {cfg.name}'s configured batches {cfg.batches}", file=sys.stderr)
