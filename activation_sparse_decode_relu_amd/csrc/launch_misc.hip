@@ -25,10 +25,11 @@ hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int
                               hipStream_t s) {
   if (B < 1 || B > kMaxTokens) return hipErrorInvalidValue;
   const dim3 grid((r + 3) / 4), block(kBlock);
-  // up to 4 tokens: 8 chunks per lane in flight; up to 16: 4 chunks (x registers for 16 tokens)
-  auto go = [&](auto nbc) -> hipError_t {
+  // Chunks of a row in flight per lane: one token, 8 (16 for rows wider than 4096, so a row is a
+  // single round of loads); up to 4 tokens, 8; up to 16, 4 (x registers for 16 tokens).
+  auto go = [&](auto nbc, auto uc) -> hipError_t {
     constexpr int NB = decltype(nbc)::value;
-    constexpr int U = NB <= 4 ? 8 : 4;
+    constexpr int U = decltype(uc)::value;
     if (pt == DT_F16 && at == DT_F16)
       hipLaunchKernelGGL((k_pred_hidden<DT_F16, DT_F16, NB, U>), grid, block, 0, s, p1, x, d, r, B, h);
     else if (pt == DT_F16 && at == DT_F32)
@@ -41,9 +42,10 @@ hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int
       return hipErrorInvalidValue;
     return hipGetLastError();
   };
-  if (B == 1) return go(std::integral_constant<int, 1>{});
-  if (B <= 4) return go(std::integral_constant<int, 4>{});
-  return go(std::integral_constant<int, 16>{});
+  using one = std::integral_constant<int, 1>;
+  if (B == 1) return d > 4096 ? go(one{}, std::integral_constant<int, 16>{}) : go(one{}, std::integral_constant<int, 8>{});
+  if (B <= 4) return go(std::integral_constant<int, 4>{}, std::integral_constant<int, 8>{});
+  return go(std::integral_constant<int, 16>{}, std::integral_constant<int, 4>{});
 }
 
 hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s) {
