@@ -8,7 +8,8 @@ captured once as a HIP graph and replayed; HIP events bracket exactly --steps
 replays.  Reported value: layers/s.  Also reported: effective HBM GB/s on the
 step's algorithmic bytes, the FFN-only tokens/s equivalent, a per-kernel
 breakdown measured with HIP events around each kernel, the roofline of the
-dominant kernel, and the CPU oracle timed on a bounded sample on the host.
+dominant kernel, the rate of a plain 1 GiB device copy on the same GPU (as
+context), and the CPU oracle timed on a bounded sample on the host.
 
     python bench.py [--config llama7b] [--mode predicted] [--batch 1] [--steps K] [--warmup W]
 """
@@ -160,6 +161,28 @@ def copy_calibration(mb: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"[bench] copy calibration: 3 copies of {mb} MiB", file=sys.stderr, flush=True)
+
+
+def copy_ceiling(mib: int = 1024, reps: int = 10) -> float:
+    """Practical HBM rate on this GPU: a plain device-to-device copy of `mib` MiB, (read + write bytes) / time.
+
+    Context for the roofline fractions, which are always taken against the published 8 TB/s peak.
+    """
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    gbps = 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, steps: int) -> dict:
@@ -406,6 +429,8 @@ def main() -> int:
         print(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, mode, B, host_sample, args.cpu_seconds)
 
+    copy_gbps = copy_ceiling()
+
     replayed = sorted({k % T for k in range(args.steps)})   # tokens the timed region ran
     mean_count = float(cnt[replayed].mean())
     out = {
@@ -427,6 +452,7 @@ def main() -> int:
                    "mean_active_neurons": round(mean_count, 1), "timing": "hipGraph per token, hipEvents"},
         "effective_hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "hbm_copy_gbps": round(copy_gbps, 1),   # context: a plain 1 GiB device copy on this GPU
         "ffn_tokens_per_s": round(layers_per_s * B / L, 1),
         "alg_bytes_per_layer_step": round(total_bytes / (args.steps * L)),
         "us_per_layer_step": round(1e6 * sec / (L * args.steps), 3),
