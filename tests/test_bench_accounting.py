@@ -1,0 +1,69 @@
+"""The benchmark's algorithmic byte accounting, checked on the CPU.
+
+The headline GB/s is bytes per layer-step divided by time, so the byte count
+is checked against totals worked out by hand from the layer shapes alone: the
+predictor's two matrices and bias, the selected neurons' rows (gate, up, down;
+int4 rows with their fp16 group scales) and fp32 biases, the dense
+pre-activation matrix in exact mode, x, y and the index list.  The selected
+counts are the expected active neurons of each workload, E|M| = sum over
+neurons of 1 - (1 - p_i)^B under the synthetic firing law, and they are pinned
+here too.
+"""
+
+import numpy as np
+import pytest
+
+import bench
+from synth import config_by_name
+from synth.layers import firing_probs
+
+# (workload, mode, batch, expected active count, MB per layer-step), to two decimals
+HAND_TOTALS = [
+    ("toy", "predicted", 1, 205, 1.51),
+    ("llama7b", "predicted", 1, 1101, 58.06),
+    ("llama7b", "exact", 1, 1101, 108.28),
+    ("llama7b", "dense", 1, 11008, 270.59),
+    ("opt30b", "predicted", 1, 1434, 114.67),
+    ("opt30b", "exact", 1, 1434, 431.75),
+    ("falcon40b", "predicted", 1, 2621, 108.24),
+    ("falcon40b", "exact", 1, 2621, 163.26),
+    ("llama70b", "predicted", 1, 2867, 216.61),
+    ("llama70b", "predicted", 4, 6943, 417.10),
+    ("llama70b", "predicted", 16, 15218, 824.31),
+    ("llama70b", "dense", 1, 28672, 1409.43),
+]
+
+
+@pytest.mark.parametrize("name,mode,B,count,mb", HAND_TOTALS)
+def test_step_bytes_match_hand_totals(name, mode, B, count, mb):
+    got = bench.step_bytes(config_by_name(name), mode, B, count) / 1e6
+    assert abs(got - mb) <= max(0.01, 1e-3 * mb), f"{name} {mode} B={B}: {got:.2f} MB, by hand {mb:.2f} MB"
+
+
+@pytest.mark.parametrize("name,B,count", [
+    ("toy", 1, 205), ("llama7b", 1, 1101), ("opt30b", 1, 1434), ("falcon40b", 1, 2621),
+    ("llama70b", 1, 2867), ("llama70b", 4, 6943), ("llama70b", 16, 15218),
+])
+def test_expected_active_counts(name, B, count):
+    p = firing_probs(config_by_name(name), 0)
+    e = float(np.sum(1.0 - (1.0 - p) ** B))
+    assert abs(e - count) <= max(1.0, 2e-3 * count), f"{name} B={B}: E|M| = {e:.1f}, expected about {count}"
+
+
+@pytest.mark.parametrize("name,mode,B", [("llama7b", "predicted", 1), ("falcon40b", "predicted", 1),
+                                         ("llama70b", "predicted", 16), ("llama7b", "exact", 1)])
+def test_phase_bytes_cover_the_step(name, mode, B):
+    """The per-kernel algorithmic bytes (the roofline's numerator) add up to the step's bytes
+    plus exactly the hand-offs between kernels: x read by a second kernel, h written and read
+    back (predicted mode), and the mask bits written (and read by the down kernel of a batch)."""
+    cfg = config_by_name(name)
+    count = 2000
+    phases = ("pred_hidden", "group", "finish") if mode == "predicted" else ("group", "finish")
+    if B > 1:
+        phases = phases[:-1] + ("down", "finish")
+    total = sum(bench.phase_bytes(cfg, mode, ph, B, count, phases) for ph in phases)
+    step = bench.step_bytes(cfg, mode, B, count)
+    handoff = cfg.d_ffn / 8 * (2 if B > 1 else 1)
+    if mode == "predicted":
+        handoff += B * cfg.d_model * 2 + 2 * B * cfg.rank * 4
+    assert abs(total - (step + handoff)) <= 1, (total, step, handoff)
