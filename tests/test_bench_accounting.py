@@ -67,3 +67,25 @@ def test_phase_bytes_cover_the_step(name, mode, B):
     if mode == "predicted":
         handoff += B * cfg.d_model * 2 + 2 * B * cfg.rank * 4
     assert abs(total - (step + handoff)) <= 1, (total, step, handoff)
+
+
+def test_counter_calibration_uses_only_the_calibration_copy(tmp_path):
+    """HBM counters are scaled by what they read for the 256 MiB calibration copy.  Other copy
+    kernels in the same process (1 GiB device copies, weight uploads) must not enter the scale."""
+    def write_csv(path, counter, rows):
+        with open(path, "w") as f:
+            f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+            for name, value in rows:
+                f.write(f'"{name}",{counter},{value}\n')
+
+    copy, kern = "__amd_rocclr_copyBuffer", "void pik::k_ffn_wave<8>(pik::GroupArgs, int)"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # calibration copy: FETCH_SIZE reads half of 256 MiB, WRITE_SIZE all of it (KiB); a 1 GiB copy
+    # reads four times as much; the kernel fetched 1000 KiB and wrote 10 KiB per dispatch
+    write_csv(fetch, "FETCH_SIZE", [(copy, 131072), (copy, 131072), (copy, 524288), (kern, 1000), (kern, 1000)])
+    write_csv(write, "WRITE_SIZE", [(copy, 262144), (copy, 1048576), (kern, 10), (kern, 10)])
+    res = bench.summarize_pmc(str(fetch), str(write), 256, "w", 1)
+    assert res["fetch_scale"] == pytest.approx(2.0) and res["write_scale"] == pytest.approx(1.0)
+    rec = res["kernels"]["w/group"]
+    assert rec["dispatches"] == 2
+    assert rec["fetch_bytes_per_launch"] == 2 * 1000 * 1024 and rec["write_bytes_per_launch"] == 10 * 1024
