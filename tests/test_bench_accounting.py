@@ -89,3 +89,16 @@ def test_counter_calibration_uses_only_the_calibration_copy(tmp_path):
     rec = res["kernels"]["w/group"]
     assert rec["dispatches"] == 2
     assert rec["fetch_bytes_per_launch"] == 2 * 1000 * 1024 and rec["write_bytes_per_launch"] == 10 * 1024
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path runs on one GPU: --gpus N > 1 exits with status 2 and says so, before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr or "one MI355X" in res.stderr
+    assert res.stdout == ""
