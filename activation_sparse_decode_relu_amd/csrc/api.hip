@@ -276,7 +276,7 @@ pi_status finish_phase(pi_ffn* h, int B, int partials, void* y, bool reduce, int
   const pi_ffn_desc& d = h->desc;
   return run_phase(h, PI_PHASE_FINISH, s, "finish", [&] {
     return pik::launch_finish(d.act_dtype, h->partial(), partials, B, d.d_model, y, list == 1 ? h->mask() : nullptr,
-                              h->L.n_words, list == 2 ? d.d_ffn : 0, idx, count, reduce, list != 0, s);
+                              d.d_ffn, list == 2 ? d.d_ffn : 0, idx, count, reduce, list != 0, s);
   });
 }
 

@@ -62,7 +62,7 @@ int wave_grid(int n, int d, int wt);   // at most (n + 7) / 8, and at most wave_
 hipError_t launch_ffn_wave(int wt, const GroupArgs& a, hipStream_t s);
 
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
-                         const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,
+                         const unsigned* mask_words, int mask_n, int iota_n, int* idx_out, int* count_out,
                          bool reduce, bool index_list, hipStream_t s);
 
 }  // namespace pik

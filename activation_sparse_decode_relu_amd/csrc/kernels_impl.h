@@ -58,20 +58,30 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
   return before + incl - v;
 }
 
-// Mask words (bit b of word w = neuron 32w + b) -> ascending int32 indices +
+// Mask word w of a layer with n neurons, with the bits of neurons >= n cleared.  Kernels that
+// write the mask a byte at a time leave the unused tail bytes of the last word untouched, and a
+// workspace shared between layers may hold another layer's bits there.
+__device__ __forceinline__ unsigned mask_word(const unsigned* words, int w, int n) {
+  const unsigned v = words[w];
+  const int rem = n - 32 * w;
+  return rem >= 32 ? v : (v & ((1u << rem) - 1u));
+}
+
+// Mask words (bit b of word w = neuron 32w + b) of n neurons -> ascending int32 indices +
 // count, by one workgroup.  Each thread owns a contiguous run of words; a scan
 // of the per-thread popcounts gives every thread its output offset, so the
 // list comes out in order.
-__device__ inline void block_compact(const unsigned* words, int n_words, int* idx, int* count) {
+__device__ inline void block_compact(const unsigned* words, int n, int* idx, int* count) {
   const int T = blockDim.x, tid = threadIdx.x;
+  const int n_words = (n + 31) / 32;
   const int wpt = (n_words + T - 1) / T;
   const int w0 = min(tid * wpt, n_words), w1 = min(w0 + wpt, n_words);
   int c = 0;
-  for (int w = w0; w < w1; ++w) c += __popc(words[w]);
+  for (int w = w0; w < w1; ++w) c += __popc(mask_word(words, w, n));
   int total;
   int pos = block_exclusive_scan(c, &total);
   for (int w = w0; w < w1; ++w) {
-    unsigned m = words[w];
+    unsigned m = mask_word(words, w, n);
     while (m) {
       const int b = __ffs((int)m) - 1;
       idx[pos++] = w * 32 + b;
@@ -521,13 +531,13 @@ __global__ __launch_bounds__(NW * WAVE) void k_ffn_group(const GroupArgs A) {
 template <int OT>
 __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partial, int NG, int B, int d,
                                                 void* __restrict__ y, const unsigned* __restrict__ mask_words,
-                                                int n_words, int iota_n, int* __restrict__ idx_out,
+                                                int mask_n, int iota_n, int* __restrict__ idx_out,
                                                 int* __restrict__ count_out, int n_col_blocks) {
   using YT = typename VecT<OT>::T;
   if ((int)blockIdx.x == n_col_blocks) {
     if (blockIdx.y != 0) return;
     if (mask_words != nullptr) {
-      block_compact(mask_words, n_words, idx_out, count_out);
+      block_compact(mask_words, mask_n, idx_out, count_out);
     } else if (iota_n > 0) {
       for (int i = threadIdx.x; i < iota_n; i += blockDim.x) idx_out[i] = i;
       if (threadIdx.x == 0) *count_out = iota_n;

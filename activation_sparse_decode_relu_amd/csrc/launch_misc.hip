@@ -58,7 +58,7 @@ hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStr
 }
 
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
-                         const unsigned* mask_words, int n_words, int iota_n, int* idx_out, int* count_out,
+                         const unsigned* mask_words, int mask_n, int iota_n, int* idx_out, int* count_out,
                          bool reduce, bool index_list, hipStream_t s) {
   const int ncol = reduce ? (d + 31) / 32 : 0;   // 32 columns per workgroup
   const int grid = ncol + (index_list ? 1 : 0);
@@ -66,10 +66,10 @@ hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, voi
   const dim3 g(grid, reduce ? B : 1);   // one row of column blocks per token
   if (ot == DT_F16)
     hipLaunchKernelGGL((k_finish<DT_F16>), g, dim3(kBlock), 0, s, partial, ng, B, d, y,
-                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
+                       index_list ? mask_words : nullptr, mask_n, iota_n, idx_out, count_out, ncol);
   else
     hipLaunchKernelGGL((k_finish<DT_F32>), g, dim3(kBlock), 0, s, partial, ng, B, d, y,
-                       index_list ? mask_words : nullptr, n_words, iota_n, idx_out, count_out, ncol);
+                       index_list ? mask_words : nullptr, mask_n, iota_n, idx_out, count_out, ncol);
   return hipGetLastError();
 }
 

@@ -26,6 +26,9 @@ from .ffn import (
     guard_band_exact,
     guard_band_predictor,
     pre_activations,
+    prob_band_exact,
+    prob_band_predictor,
+    PROB_LAMBDA,
     predictor_hidden,
     predictor_logits,
     predicted_mask,
@@ -49,6 +52,9 @@ __all__ = [
     "guard_band_exact",
     "guard_band_predictor",
     "pre_activations",
+    "prob_band_exact",
+    "prob_band_predictor",
+    "PROB_LAMBDA",
     "predictor_hidden",
     "predictor_logits",
     "predicted_mask",

@@ -260,6 +260,62 @@ def guard_band_predictor(x, p1, p2, b_p) -> np.ndarray:
     return GUARD_SAFETY * bound
 
 
+# ----------------------------------------------------------------------------
+# Probabilistic guard bands (Higham and Mary, "A New Approach to Probabilistic
+# Rounding Error Analysis", SIAM J. Sci. Comput. 41(5), 2019): rounding errors
+# are modelled as independent, mean-zero random variables, each at most u times
+# the value being rounded.  To first order, the error of an fp32 value built
+# from m roundings is then a sum of m independent bounded mean-zero terms, and
+# Hoeffding's inequality bounds it by lambda * u * sqrt(sum of squared term
+# bounds) except with probability 2 exp(-lambda^2 / 2).  Every partial sum of a
+# dot product, in any order, is at most the sum of the absolute terms, which
+# bounds each term.  For the predictor logit all roundings (those of h, carried
+# through P2, and those of z's own dot product) are bounded together.
+# ----------------------------------------------------------------------------
+
+PROB_LAMBDA = 10.0   # 2 exp(-50) ~ 4e-22 per value: no realistic test meets a miss
+
+
+def _rounding_events(k: int) -> int:
+    """Roundings an fp32 dot product of k terms plus a bias may take: one per product and one per
+    addition (products of two fp16 values are exact in fp32; counting them is harmless)."""
+    return 2 * k + 2
+
+
+def prob_band_exact(x, w_rows, b, lam: float = PROB_LAMBDA) -> np.ndarray:
+    """Band for g_i = x . w_i + b_i in fp32: lambda u sqrt(m) (|x|.|w_i| + |b_i|), plus the
+    second-order term (m u)^2 times the same magnitude."""
+    xx = np.abs(_f64(x))
+    w = np.abs(np.asarray(w_rows, dtype=np.float64))
+    m = _rounding_events(w.shape[1])
+    mag = xx @ w.T + np.abs(np.asarray(b, dtype=np.float64))
+    u = UNIT_ROUNDOFF_F32
+    return (lam * u * math.sqrt(m) + (m * u) ** 2) * mag
+
+
+def prob_band_predictor(x, p1, p2, b_p, lam: float = PROB_LAMBDA) -> np.ndarray:
+    """Band for z_i = ReLU(x P1^T) P2_i + b_p,i with h and z accumulated in fp32.
+
+    First order: z_hat - z = sum_j P2_ij dh_j + e_i, dh_j a sum of m_h roundings each at most
+    u A_j (A_j = |x|.|P1_j|), e_i a sum of m_z roundings each at most u C_i
+    (C_i = |P2_i|.|h| + |b_p,i|).  Hoeffding over all of them:
+    lambda u sqrt(m_h sum_j P2_ij^2 A_j^2 + m_z C_i^2).  Second order: (m_h u)^2 |P2_i|.A
+    + (m_z u)^2 C_i.
+    """
+    xx = _f64(x)
+    p1a = np.asarray(p1, dtype=np.float64)
+    p2a = np.asarray(p2, dtype=np.float64)
+    d, r = p1a.shape[1], p1a.shape[0]
+    m_h, m_z = _rounding_events(d), _rounding_events(r)
+    u = UNIT_ROUNDOFF_F32
+    A = np.abs(xx) @ np.abs(p1a).T                          # [B][r]
+    h = np.maximum(xx @ p1a.T, 0.0)
+    C = h @ np.abs(p2a).T + np.abs(np.asarray(b_p, dtype=np.float64))
+    first = lam * u * np.sqrt(m_h * ((A * A) @ (p2a * p2a).T) + m_z * C * C)
+    second = (m_h * u) ** 2 * (A @ np.abs(p2a).T) + (m_z * u) ** 2 * C
+    return first + second
+
+
 def certain_union(values, band, threshold: float = 0.0):
     """(certainly_on, certainly_off) for the batch-union decision values > threshold."""
     v = _f64(values)

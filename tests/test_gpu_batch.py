@@ -127,12 +127,15 @@ def test_random_layer_batched(B, mode):
     check_idx_valid(idx, count, layer.d_ffn)
     if mode == "predicted":
         vals = oracle.predictor_logits(x, layer.p1, layer.p2, layer.b_p)
-        band = oracle.guard_band_predictor(x, layer.p1, layer.p2, layer.b_p)
+        band = oracle.GUARD_SAFETY * oracle.prob_band_predictor(x, layer.p1, layer.p2, layer.b_p)
+        rig = oracle.guard_band_predictor(x, layer.p1, layer.p2, layer.b_p) / oracle.GUARD_SAFETY
         thr = oracle.threshold_logit(layer.tau)
         pidx, _, z = run_predict(h, x)
         assert np.array_equal(pidx, idx)
         assert np.array_equal(idx, np.flatnonzero((z > np.float32(thr)).any(axis=0)))   # own decisions
-        assert np.all(np.abs(z.astype(np.float64) - vals) <= band / oracle.GUARD_SAFETY), "logit outside the fp32 bound"
+        err = np.abs(z.astype(np.float64) - vals)
+        assert np.all(err <= rig), "logit outside the rigorous fp32 bound"
+        assert np.all(err <= band / oracle.GUARD_SAFETY), "logit outside the probabilistic fp32 bound"
         # the batch's list is the union of the per-token lists
         union = set()
         for t in range(B):
@@ -141,7 +144,7 @@ def test_random_layer_batched(B, mode):
     else:
         pre = oracle.dense_weights(layer.w_gate, layer.s_gate)
         vals = x.astype(np.float64) @ pre.T + layer.b
-        band, thr = oracle.guard_band_exact(x, pre, layer.b), 0.0
+        band, thr = oracle.GUARD_SAFETY * oracle.prob_band_exact(x, pre, layer.b), 0.0
     check_decisions(idx, layer.d_ffn, vals, band, thr)
     ref = oracle.forward_masked(layer, x, idx)["y64"]
     assert rel_l2_rows(y, ref).max() <= 1e-3

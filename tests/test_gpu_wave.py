@@ -147,7 +147,7 @@ def test_random_llama7b_layer_wave_and_graph_replay():
     idx, count, y = run_forward(h, x, "predicted")
     check_idx_valid(idx, count, layer.d_ffn)
     zo = oracle.predictor_logits(x, layer.p1, layer.p2, layer.b_p)
-    band = oracle.guard_band_predictor(x, layer.p1, layer.p2, layer.b_p)
+    band = oracle.GUARD_SAFETY * oracle.prob_band_predictor(x, layer.p1, layer.p2, layer.b_p)
     check_decisions(idx, layer.d_ffn, zo, band, oracle.threshold_logit(layer.tau))
     ref = oracle.forward_masked(layer, x, idx)["y64"]
     assert rel_l2_rows(y, ref).max() <= 1e-3
@@ -186,3 +186,32 @@ def test_launch_plan_reports_the_kernels():
     assert h.launch_plan(1, "exact") == ("group", "finish")
     assert h.launch_plan(16, "dense") == ("group", "down", "finish")
     h.close()
+
+
+@pytest.mark.parametrize("d,w_dtype", [(512, "f16"), (8192, "f16"), (4096, "q4g32")])
+def test_shared_workspace_smaller_layer_after_larger(d, w_dtype):
+    """A layer whose n leaves the last mask word partly unused (n % 32 = 8), run on a workspace a
+    larger layer has just filled with selected neurons: its list must not pick up the larger
+    layer's bits beyond n."""
+    pi = _pi()
+    announce(f"shared workspace: n=2000 then n=1000, d={d} {w_dtype}")
+    big = make_lattice_layer(d, 2000, 128, True, w_dtype=w_dtype, seed=91)
+    big.b_p = np.full(2000, 1000.0, dtype=np.float32)     # every neuron of the larger layer fires
+    small = make_lattice_layer(d, 1000, 128, True, w_dtype=w_dtype, seed=92)
+    hb = pi.upload_layer(big, "cuda", max_batch=1)
+    hs = pi.upload_layer(small, "cuda", max_batch=1, workspace=hb.workspace)
+    xb = make_lattice_tokens(d, 1, seed=93)
+    idx_b, count_b, _ = run_forward(hb, xb, "predicted")
+    assert count_b == 2000
+    for t in range(2):
+        x = make_lattice_tokens(d, 1, seed=94 + t)
+        ref = oracle.forward(small, x, "predicted")
+        idx, count, y = run_forward(hs, x, "predicted")
+        check_idx_valid(idx, count, 1000)
+        assert count == ref["count"] and np.array_equal(idx, ref["idx"]), f"token {t}"
+        assert _bitwise(y, ref["y"]), f"token {t}"
+        pidx, pcount, _ = run_predict(hs, x)
+        assert pcount == ref["count"] and np.array_equal(pidx, ref["idx"])
+        run_forward(hb, xb, "predicted")                   # the larger layer again, in between
+    hs.close()
+    hb.close()

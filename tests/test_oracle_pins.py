@@ -348,3 +348,163 @@ def test_round_to_act_is_round_half_even():
     # 2049 lies halfway between the fp16 neighbours 2048 and 2050; ties go to even (2048)
     y = oracle.round_to_act(np.array([2049.0, 2051.0, 1.0 + 2.0 ** -11]), "f16")
     assert y.tolist() == [2048.0, 2052.0, 1.0]
+
+
+# ----------------------------------------------------------------------------
+# forward_masked: the sparse operator on a given list, pinned on its own
+# ----------------------------------------------------------------------------
+
+def test_forward_masked_golden_lists():
+    """Each hand-worked case's list through forward_masked gives the hand-worked y."""
+    fx = json.load(open(os.path.join(GOLDEN, "tiny_ffn.json")))
+    x_all = np.array(fx["x"], dtype=np.float64)
+    for case in fx["cases"]:
+        layer = _layer(gated=case["gated"],
+                       w_gate=np.array(fx["w_gate"], float) if case["gated"] else None,
+                       w_up=np.array(fx["w_up"], float), w_down_t=np.array(fx["w_down_t"], float),
+                       b=np.array(fx["b"], float), tau=case["tau"])
+        out = oracle.forward_masked(layer, x_all[case["tokens"]], case["idx"])
+        assert np.array_equal(out["y64"], np.array(case["y"], dtype=np.float64)), case
+
+
+def _nibble_values(packed_row):
+    """Signed int4 values of one packed row, decoded from the format statement in the test."""
+    vals = []
+    for byte in packed_row:
+        for nib in (int(byte) & 0xF, int(byte) >> 4):      # low nibble first: the even element
+            vals.append(nib - 16 if nib >= 8 else nib)
+    return vals
+
+
+def _brute_masked(x, wg, wu, wd, b, gated, idx):
+    """y_t = sum over the listed neurons of ReLU(g) u W_downT, in Fraction arithmetic."""
+    F = Fraction
+    ys = []
+    for xt in x:
+        xt = [F(v) for v in xt]
+        y = [F(0)] * len(wd[0])
+        for i in idx:
+            pre = wg[i] if gated else wu[i]
+            g = sum(xt[k] * pre[k] for k in range(len(xt))) + F(b[i])
+            u = sum(xt[k] * wu[i][k] for k in range(len(xt))) if gated else F(1)
+            a = max(g, F(0)) * u
+            y = [y[c] + a * wd[i][c] for c in range(len(y))]
+        ys.append(y)
+    return ys
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_forward_masked_rational_subsets(gated, seed):
+    rng = np.random.default_rng(300 + seed)
+    d, n, B = 6, 9, 2
+    wg = _dyadic(rng, (n, d)) if gated else None
+    wu, wd, b, x = _dyadic(rng, (n, d)), _dyadic(rng, (n, d)), _dyadic(rng, n), _dyadic(rng, (B, d))
+    layer = _layer(gated=gated, w_gate=wg, w_up=wu, w_down_t=wd, b=b)
+    F = Fraction
+    fr = (lambda m: [[F(v) for v in row] for row in m.tolist()])
+    for k in (0, 1, 3, n):
+        for _ in range(3):
+            idx = sorted(rng.choice(n, size=k, replace=False).tolist())
+            got = oracle.forward_masked(layer, x, idx)["y64"]
+            ref = _brute_masked(x.tolist(), None if wg is None else fr(wg), fr(wu), fr(wd), b.tolist(), gated, idx)
+            assert [[F(v) for v in row] for row in got] == ref, idx
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_forward_masked_int4_distinct_scales(gated):
+    """int4 rows with different scales per matrix and per group: a swap of the gate and up rows,
+    of their scales, or a bias on u instead of g changes y."""
+    rng = np.random.default_rng(310 + int(gated))
+    d, n, B = 64, 6, 2
+    mats, scales = [], []
+    for m in range(3):
+        q = rng.integers(-8, 8, size=(n, d))
+        s = (np.float16(2.0) ** rng.integers(-3, 2, size=(n, d // 32))).astype(np.float16) * np.float16(1 + m)
+        mats.append(pack_nibbles(q))
+        scales.append(s)
+    b = _dyadic(rng, n)
+    x = _dyadic(rng, (B, d))
+    layer = _layer(gated=gated, w_gate=mats[0] if gated else None, s_gate=scales[0] if gated else None,
+                   w_up=mats[1], s_up=scales[1], w_down_t=mats[2], s_down=scales[2], b=b, d_ffn=n)
+    F = Fraction
+
+    def rows(m):
+        out = []
+        for i in range(n):
+            vals = _nibble_values(mats[m][i])
+            out.append([F(v) * F(float(scales[m][i][k // 32])) for k, v in enumerate(vals)])
+        return out
+
+    wg, wu, wd = rows(0) if gated else None, rows(1), rows(2)
+    for idx in ([0], [1, 4], list(range(n))):
+        got = oracle.forward_masked(layer, x, idx)["y64"]
+        ref = _brute_masked(x.tolist(), wg, wu, wd, b.tolist(), gated, idx)
+        assert [[F(v) for v in row] for row in got] == ref, idx
+    # and it agrees with forward() on forward()'s own list
+    for mode in ("exact", "dense"):
+        full = oracle.forward(layer, x, mode)
+        assert np.array_equal(oracle.forward_masked(layer, x, full["idx"])["y64"], full["y64"])
+
+
+def test_forward_masked_matches_forward_on_its_list():
+    rng = np.random.default_rng(320)
+    d, n, r = 32, 40, 8
+    for gated in (False, True):
+        layer = _layer(gated=gated, w_gate=_dyadic(rng, (n, d)) if gated else None, w_up=_dyadic(rng, (n, d)),
+                       w_down_t=_dyadic(rng, (n, d)), b=_dyadic(rng, n), p1=_dyadic(rng, (r, d)),
+                       p2=_dyadic(rng, (n, r)), b_p=_dyadic(rng, n))
+        x = _dyadic(rng, (3, d))
+        for mode in ("predicted", "exact", "dense"):
+            full = oracle.forward(layer, x, mode)
+            assert np.array_equal(oracle.forward_masked(layer, x, full["idx"])["y64"], full["y64"]), (gated, mode)
+
+
+# ----------------------------------------------------------------------------
+# The probabilistic bands bound real fp32 evaluations in several orders, and are
+# tighter than the rigorous ones
+# ----------------------------------------------------------------------------
+
+def _f32_orders(x, w, b, rng):
+    """fp32 evaluations of x w^T + b: sequential, reversed, a random order, and BLAS's own."""
+    k = x.shape[1]
+    out = [_f32_sequential(x, w, b), _f32_sequential(x[:, ::-1], w[:, ::-1], b)]
+    perm = rng.permutation(k)
+    out.append(_f32_sequential(x[:, perm], w[:, perm], b))
+    out.append(x.astype(np.float32) @ w.astype(np.float32).T + b.astype(np.float32))
+    return out
+
+
+def test_prob_band_bounds_fp32_exact():
+    rng = np.random.default_rng(21)
+    d, n = 2048, 200
+    w = (rng.standard_normal((n, d)) / math.sqrt(d)).astype(np.float16)
+    b = rng.standard_normal(n).astype(np.float32)
+    x = rng.standard_normal((3, d)).astype(np.float16)
+    g64 = x.astype(np.float64) @ w.astype(np.float64).T + b
+    band = oracle.prob_band_exact(x, w, b)
+    assert np.all(band <= oracle.guard_band_exact(x, w, b) / oracle.GUARD_SAFETY)
+    worst = 0.0
+    for g32 in _f32_orders(x, w, b, rng):
+        err = np.abs(g32.astype(np.float64) - g64)
+        assert np.all(err <= band)
+        worst = max(worst, float((err / band).max()))
+    assert worst > 1e-4   # the errors are real, not zero: the check has something to bound
+
+
+def test_prob_band_bounds_fp32_predictor():
+    rng = np.random.default_rng(22)
+    d, r, n = 1024, 128, 300
+    p1 = (rng.standard_normal((r, d)) / math.sqrt(d)).astype(np.float16)
+    p2 = (rng.standard_normal((n, r)) / math.sqrt(r)).astype(np.float16)
+    b_p = rng.standard_normal(n).astype(np.float32)
+    x = rng.standard_normal((2, d)).astype(np.float16)
+    z64 = oracle.predictor_logits(x, p1, p2, b_p)
+    band = oracle.prob_band_predictor(x, p1, p2, b_p)
+    assert np.all(band <= oracle.guard_band_predictor(x, p1, p2, b_p) / oracle.GUARD_SAFETY)
+    zero = np.zeros(r, dtype=np.float32)
+    for h32 in _f32_orders(x, p1, zero, rng):
+        h32 = np.maximum(h32, 0).astype(np.float32)
+        for z32 in _f32_orders(h32, p2, b_p, rng):
+            assert np.all(np.abs(z32.astype(np.float64) - z64) <= band)
+
