@@ -2,12 +2,15 @@
 // workspace layout and the kernel sequence of each call.
 //
 // Sequences (PowerInfer paper explainer, section "GPU-CPUハイブリッドアーキテクチャ",
-// inference flow: predict, then compute only the predicted neurons):
-//   predict            pred_hidden -> ffn_group(mask only) -> finish(index list)
-//   forward PREDICTED  pred_hidden -> ffn_group(predictor mask) -> finish
-//   forward EXACT      ffn_group(dense pre-activation mask) -> finish
-//   forward DENSE      ffn_group(every neuron) -> finish
-//   forward_masked     ffn_group(caller's list) -> finish
+// inference flow: predict, then compute only the predicted neurons).  One token with fp16
+// activations and predictor and fp16 or int4 rows (the split path):
+//   predict            pred_hidden -> act(mask only) -> down(index list only)
+//   forward PREDICTED  pred_hidden -> act(predictor mask) -> down
+//   forward EXACT      act(dense pre-activation mask) -> down
+//   forward DENSE      act(every neuron) -> down
+//   forward_masked     act(caller's list) -> down
+// Batches of 2..16 on the matrix-core path (group -> down -> finish) and every other case on
+// the vector path (group -> finish) follow the same pattern, with the mask source first.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -49,8 +52,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t h, mask, idx, count, abuf, partial, total;
-  int group, waves, n_groups, n_words, max_partials;
+  size_t h, mask, idx, count, abuf, partial, tickets, total;
+  int group, waves, n_groups, n_words, max_partials, slices;
 };
 
 // Neurons per group workgroup and waves per workgroup for a layer.  Small
@@ -79,13 +82,19 @@ Layout layout_for(const pi_ffn_desc& d) {
   L.mask = off;    off = align_up(off + sizeof(unsigned) * (size_t)L.n_words);
   L.idx = off;     off = align_up(off + sizeof(int) * n);
   L.count = off;   off = align_up(off + sizeof(int));
-  // activations of the batched matrix-core path: a[neuron][16] fp32
-  L.abuf = off;    off = align_up(off + (d.max_batch > 1 ? sizeof(float) * n * pik::kMaxTokens : 0));
-  // partials: one [B][d] block per group workgroup, or per down chunk on the batched path
+  // activations handed from the group (or act) kernel to the down kernel: a[neuron][16] fp32 on
+  // the batched matrix-core path, a[neuron] on the one-token split path
+  L.abuf = off;    off = align_up(off + sizeof(float) * n * (d.max_batch > 1 ? pik::kMaxTokens : 1));
+  // partials: one [B][d] block per group workgroup, or per down chunk on the batched path;
+  // [chunks][d] on the split path
   L.max_partials = L.n_groups;
   if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
   L.max_partials = std::max(L.max_partials, pik::wave_grid(d.d_ffn, d.d_model, d.w_dtype));
-  L.partial = off; off = align_up(off + sizeof(float) * (size_t)L.max_partials * B * dm);
+  const size_t split_part = (size_t)pik::split_chunks(d.w_dtype, d.d_model) * dm;
+  L.partial = off; off = align_up(off + sizeof(float) * std::max((size_t)L.max_partials * B * dm, split_part));
+  // the split path's ticket counter per column slice (zero between calls)
+  L.slices = pik::split_slices(d.w_dtype, d.d_model);
+  L.tickets = off; off = align_up(off + sizeof(unsigned) * (size_t)L.slices * pik::kTicketStride);
   L.total = off;
   return L;
 }
@@ -152,6 +161,7 @@ struct pi_ffn {
   int* count() const { return reinterpret_cast<int*>(ws + L.count); }
   float* partial() const { return reinterpret_cast<float*>(ws + L.partial); }
   float* abuf() const { return reinterpret_cast<float*>(ws + L.abuf); }
+  unsigned* tickets() const { return reinterpret_cast<unsigned*>(ws + L.tickets); }
 };
 
 namespace {
@@ -228,15 +238,16 @@ pik::GroupArgs group_args(const pi_ffn* h, const void* x, int B) {
 
 // Which kernels a call runs.
 struct Plan {
-  bool batched;   // matrix-core batch path: group + down kernels
-  bool wave;      // wave-independent one-token kernel
+  bool batched;   // matrix-core batch path: group + down + finish kernels
+  bool split;     // one-token split path: act + down kernels, no finish
 };
 
 Plan plan_for(const pi_ffn* h, int mode, int B) {
+  (void)mode;
   const pi_ffn_desc& d = h->desc;
   Plan p{};
   p.batched = pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank);
-  p.wave = !p.batched && pik::wave_supported(d.w_dtype, d.act_dtype, d.p_dtype, mode, B, d.d_model, d.rank);
+  p.split = !p.batched && pik::split_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank);
   return p;
 }
 
@@ -260,14 +271,33 @@ pi_status group_phase(pi_ffn* h, int mode, const Plan& plan, const pik::GroupArg
     return run_phase(h, PI_PHASE_DOWN, s, "ffn_bdown",
                      [&] { return pik::launch_ffn_bdown(mode, a, h->abuf(), chunks, s); });
   }
-  if (plan.wave) {
-    *partials = pik::wave_grid(d.d_ffn, d.d_model, d.w_dtype);
-    return run_phase(h, PI_PHASE_GROUP, s, "ffn_wave",
-                     [&] { return pik::launch_ffn_wave(d.w_dtype, a, s); });
-  }
   *partials = h->L.n_groups;
   return run_phase(h, PI_PHASE_GROUP, s, "ffn_group",
                    [&] { return pik::launch_ffn_group(d.w_dtype, d.act_dtype, mode, a, s); });
+}
+
+// The one-token split path: act, then down (y, and the index list when idx / count are given).
+pi_status split_phases(pi_ffn* h, int mode, const pik::GroupArgs& a, void* y, int* idx, int* count, hipStream_t s) {
+  const pi_ffn_desc& d = h->desc;
+  pi_status st = run_phase(h, PI_PHASE_GROUP, s, "act", [&] { return pik::launch_act(d.w_dtype, mode, a, h->abuf(), s); });
+  if (st != PI_OK) return st;
+  pik::DownArgs D{};
+  D.abuf = h->abuf();
+  D.w_down_t = h->w.w_down_t;
+  D.s_down = static_cast<const _Float16*>(h->w.s_down);
+  D.mask = h->mask();
+  D.list = a.list;
+  D.list_count = a.list_count;
+  D.partial = h->partial();
+  D.tickets = h->tickets();
+  D.y = y;
+  D.idx_out = idx;
+  D.count_out = count;
+  D.n = d.d_ffn;
+  D.d = d.d_model;
+  D.chunks = pik::split_chunks(d.w_dtype, d.d_model);
+  D.do_down = a.mask_only ? 0 : 1;
+  return run_phase(h, PI_PHASE_DOWN, s, "down", [&] { return pik::launch_down(d.w_dtype, mode, D, s); });
 }
 
 // reduce: sum the partials into y; list: 0 = none, 1 = compact the mask words, 2 = 0..n-1
@@ -321,6 +351,7 @@ pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights, 
   // Clear the mask words once so a predict() before any forward() never reads garbage.
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pik::launch_fill_u32(h->mask(), L.n_words, 0u, s);
+  if (e == hipSuccess) e = pik::launch_fill_u32(h->tickets(), L.slices * pik::kTicketStride, 0u, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete h;
@@ -352,6 +383,10 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, 
   int partials = 0;
   const Plan plan = plan_for(h, pik::MODE_PRED, batch);
   if ((st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
+  if (plan.split) {
+    if ((st = split_phases(h, pik::MODE_PRED, a, nullptr, idx, count, s)) != PI_OK) return st;
+    return ok();
+  }
   if ((st = group_phase(h, pik::MODE_PRED, plan, a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, nullptr, false, 1, idx, count, s)) != PI_OK) return st;
   return ok();
@@ -391,6 +426,11 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
   int partials = 0;
   const Plan plan = plan_for(h, mode, batch);
   if (mode == pik::MODE_PRED && (st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
+  if (plan.split) {
+    if ((st = split_phases(h, mode, a, y, want_list ? idx : nullptr, want_list ? count : nullptr, s)) != PI_OK)
+      return st;
+    return ok();
+  }
   if ((st = group_phase(h, mode, plan, a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
   return ok();
@@ -407,7 +447,12 @@ pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const i
   a.list = idx;
   a.list_count = count;
   int partials = 0;
-  if ((st = group_phase(h, pik::MODE_LIST, plan_for(h, pik::MODE_LIST, batch), a, s, &partials)) != PI_OK) return st;
+  const Plan plan = plan_for(h, pik::MODE_LIST, batch);
+  if (plan.split) {
+    if ((st = split_phases(h, pik::MODE_LIST, a, y, nullptr, nullptr, s)) != PI_OK) return st;
+    return ok();
+  }
+  if ((st = group_phase(h, pik::MODE_LIST, plan, a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, y, true, 0, nullptr, nullptr, s)) != PI_OK) return st;
   return ok();
 }
@@ -427,9 +472,10 @@ pi_status pi_ffn_launch_plan(const pi_ffn* h, int32_t batch, int32_t mask_mode, 
     default: return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
   }
   const Plan p = plan_for(h, mode, batch);
-  uint32_t bits = (1u << PI_PHASE_GROUP) | (1u << PI_PHASE_FINISH);
+  uint32_t bits = 1u << PI_PHASE_GROUP;
+  if (!p.split) bits |= 1u << PI_PHASE_FINISH;
   if (mode == pik::MODE_PRED) bits |= 1u << PI_PHASE_PRED_HIDDEN;
-  if (p.batched) bits |= 1u << PI_PHASE_DOWN;
+  if (p.batched || p.split) bits |= 1u << PI_PHASE_DOWN;
   *plan = bits;
   return ok();
 }

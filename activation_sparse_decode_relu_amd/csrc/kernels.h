@@ -61,6 +61,32 @@ bool wave_supported(int wt, int at, int pt, int mode, int B, int d, int r);
 int wave_grid(int n, int d, int wt);   // at most (n + 7) / 8, and at most wave_grid(n, 512, fp16)
 hipError_t launch_ffn_wave(int wt, const GroupArgs& a, hipStream_t s);
 
+// The one-token split path (fp16 activations, fp16 or int4 weights, fp16 predictor, batch 1):
+// k_act writes the mask bits and a[neuron] (fp32) into abuf; k_down sums a * W_down^T rows over
+// (column slice, list chunk) tiles, the last tile of each slice adding the chunks' partials into
+// y, and writes the index list.
+struct DownArgs {
+  const float* abuf;        // a[neuron], fp32
+  const void* w_down_t;     // [n][d] rows
+  const _Float16* s_down;   // int4: fp16 [n][d/32]
+  const unsigned* mask;     // MODE_PRED / MODE_EXACT
+  const int* list;          // MODE_LIST
+  const int* list_count;    // MODE_LIST
+  float* partial;           // [chunks][d]
+  unsigned* tickets;        // [slices * kTicketStride], zero between calls
+  void* y;                  // [d] act dtype (fp16)
+  int* idx_out;             // optional
+  int* count_out;           // optional
+  int n, d, chunks, do_down;
+};
+constexpr int kMaxDnChunks = 32;   // list chunks per column slice (partials the last tile adds)
+constexpr int kTicketStride = 64;  // one ticket per 256 bytes: tickets of different slices share no line
+bool split_supported(int wt, int at, int pt, int B, int d, int r);
+int split_slices(int wt, int d);
+int split_chunks(int wt, int d);
+hipError_t launch_act(int wt, int mode, const GroupArgs& a, float* abuf, hipStream_t s);
+hipError_t launch_down(int wt, int mode, const DownArgs& D, hipStream_t s);
+
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
                          const unsigned* mask_words, int mask_n, int iota_n, int* idx_out, int* count_out,
                          bool reduce, bool index_list, hipStream_t s);

@@ -1,0 +1,105 @@
+// Launchers of the one-token split path (k_act, then k_down).
+#include <algorithm>
+
+#include "kernels_split.h"
+
+namespace pik {
+
+namespace {
+
+constexpr int kNPW = 8;   // neurons per k_act wave: one mask byte
+
+int epc_of(int wt) { return wt == DT_Q4 ? 32 : (wt == DT_F16 ? 8 : 4); }
+
+// Chunks of 16 bytes per lane in a full weight row (0 if the row does not split evenly).
+int row_cpl(int wt, int d) {
+  const int per = WAVE * epc_of(wt);
+  return d % per == 0 ? d / per : 0;
+}
+
+}  // namespace
+
+bool split_supported(int wt, int at, int pt, int B, int d, int r) {
+  if (B != 1 || at != DT_F16 || (r > 0 && pt != DT_F16)) return false;
+  const int cpl = row_cpl(wt, d);
+  if (wt == DT_F16) return cpl >= 1 && cpl <= 16;   // d = 512 .. 8192 in steps of 512
+  if (wt == DT_Q4) return cpl >= 1 && cpl <= 4;     // d = 2048 .. 8192 in steps of 2048
+  return false;
+}
+
+int split_slices(int wt, int d) {
+  const int sw = wt == DT_Q4 ? dn_slice_cols<DT_Q4>() : dn_slice_cols<DT_F16>();
+  return (d + sw - 1) / sw;
+}
+
+int split_chunks(int wt, int d) {
+  // about 512 down tiles (two per compute unit), at most kMaxDnChunks partials per slice: the last
+  // tile of a slice reads them all in one round of loads
+  const int s = split_slices(wt, d);
+  return std::max(1, std::min(kMaxDnChunks, (512 + s - 1) / s));
+}
+
+template <int WT, int MODE>
+static hipError_t act_cpl(const GroupArgs& a, float* abuf, int cpl, hipStream_t s) {
+  const int waves = (a.n + kNPW - 1) / kNPW;
+  const dim3 grid((waves + kActWaves - 1) / kActWaves), block(kActWaves * WAVE);
+  switch (cpl) {
+#define PIK_ACT(C) \
+  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW>), grid, block, 0, s, a, abuf); break;
+    PIK_ACT(1) PIK_ACT(2) PIK_ACT(3) PIK_ACT(4)
+    default:
+      if constexpr (WT == DT_F16) {
+        switch (cpl) {
+          PIK_ACT(5) PIK_ACT(6) PIK_ACT(7) PIK_ACT(8) PIK_ACT(9) PIK_ACT(10) PIK_ACT(11) PIK_ACT(12)
+          PIK_ACT(13) PIK_ACT(14) PIK_ACT(15) PIK_ACT(16)
+          default: return hipErrorInvalidValue;
+        }
+      } else {
+        return hipErrorInvalidValue;
+      }
+#undef PIK_ACT
+  }
+  return hipGetLastError();
+}
+
+template <int WT>
+static hipError_t act_mode(int mode, const GroupArgs& a, float* abuf, int cpl, hipStream_t s) {
+  switch (mode) {
+    case MODE_PRED: return act_cpl<WT, MODE_PRED>(a, abuf, cpl, s);
+    case MODE_EXACT: return act_cpl<WT, MODE_EXACT>(a, abuf, cpl, s);
+    case MODE_DENSE: return act_cpl<WT, MODE_DENSE>(a, abuf, cpl, s);
+    case MODE_LIST: return act_cpl<WT, MODE_LIST>(a, abuf, cpl, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_act(int wt, int mode, const GroupArgs& a, float* abuf, hipStream_t s) {
+  const int cpl = row_cpl(wt, a.d);
+  if (wt == DT_F16) return act_mode<DT_F16>(mode, a, abuf, cpl, s);
+  if (wt == DT_Q4) return act_mode<DT_Q4>(mode, a, abuf, cpl, s);
+  return hipErrorInvalidValue;
+}
+
+template <int WT>
+static hipError_t down_mode(int mode, const DownArgs& D, dim3 grid, hipStream_t s) {
+  constexpr int U = WT == DT_Q4 ? 4 : 8;
+  const dim3 block(kDnThreads);
+  switch (mode) {
+    case MODE_PRED: hipLaunchKernelGGL((k_down<WT, MODE_PRED, U>), grid, block, 0, s, D); break;
+    case MODE_EXACT: hipLaunchKernelGGL((k_down<WT, MODE_EXACT, U>), grid, block, 0, s, D); break;
+    case MODE_DENSE: hipLaunchKernelGGL((k_down<WT, MODE_DENSE, U>), grid, block, 0, s, D); break;
+    case MODE_LIST: hipLaunchKernelGGL((k_down<WT, MODE_LIST, U>), grid, block, 0, s, D); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down(int wt, int mode, const DownArgs& D, hipStream_t s) {
+  // an index-list-only call (predict) runs one tile, which writes the list and count
+  const dim3 grid = D.do_down ? dim3(split_slices(wt, D.d), D.chunks) : dim3(1, 1);
+  if (wt == DT_F16) return down_mode<DT_F16>(mode, D, grid, s);
+  if (wt == DT_Q4) return down_mode<DT_Q4>(mode, D, grid, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pik

@@ -11,7 +11,7 @@ breakdown measured with HIP events around each kernel, the roofline of the
 dominant kernel, the rate of a plain 1 GiB device copy on the same GPU (as
 context), and the CPU oracle timed on a bounded sample on the host.
 
-    python bench.py [--config llama7b] [--mode predicted] [--batch 1] [--steps K] [--warmup W]
+    python bench.py [--config llama70b] [--mode predicted] [--batch 1] [--steps K] [--warmup W]
 """
 
 import argparse
@@ -66,15 +66,19 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases) -> float
     pred_hidden: P1, x, h.  group: the mask source (P2 + b_p, or the dense
     pre-activation rows + b), the selected rows of every matrix the mode reads
     with their bias, x and the mask bits; its partial-sum writes are scratch
-    and not counted.  On the batched path the group kernel reads the selected
+    and not counted.  Where a down kernel runs, the group kernel reads only the
     gate/up rows and the down kernel the selected down rows (the activations
-    handed between them are scratch).  finish: y and the index list.
+    handed between them are scratch).  The finish kernel writes y and the index
+    list; on the one-token split path (a down kernel and no finish kernel) the
+    down kernel writes them, reading the mask bits to find the list.
     `phases` is the library's launch plan for the call.
     """
     d, n, r = cfg.d_model, cfg.d_ffn, cfg.rank
     ea, rb = esize(cfg.act_dtype), row_bytes(cfg.w_dtype, d)
+    split = "down" in phases and "finish" not in phases
     down = 0 if "down" in phases else 1      # down rows read by the group kernel
     hidden = r * d * esize(cfg.p_dtype) + B * d * ea + B * r * 4
+    out = B * d * ea + 4 * count             # y and the index list
     if phase == "pred_hidden":
         return hidden
     if phase == "group":
@@ -84,11 +88,14 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases) -> float
                     + xb)
         if mode == "exact":
             return n * rb + 4 * n + count * ((down + cfg.gated) * rb) + xb
+        if split:
+            return count * ((1 + cfg.gated) * rb + 4) + B * d * ea
         return count * ((1 + down + cfg.gated) * rb + 4) + xb
     if phase == "down":
-        return count * rb + n / 8
+        mask = 0 if mode == "dense" else n / 8
+        return count * rb + mask + (out if split else 0)
     if phase == "finish":
-        return B * d * ea + 4 * count
+        return out
     raise KeyError(phase)
 
 
@@ -214,7 +221,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, 
     w_scale = expect_kib / (sum(big_w) / len(big_w)) if big_w else None
     out = {"copy_mib": copy_mib, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     phase_of = {"k_pred_hidden": "pred_hidden", "k_ffn_group": "group", "k_ffn_bgroup": "group",
-                "k_ffn_wave": "group", "k_ffn_bdown": "down", "k_finish": "finish"}
+                "k_act": "group", "k_ffn_bdown": "down", "k_down": "down", "k_finish": "finish"}
     for name, vals in fetch.items():
         phase = next((p for k, p in phase_of.items() if k in name), None)
         if phase is None or f_scale is None:
@@ -230,37 +237,55 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, 
 
 
 def cpu_baseline(cfg, mode: str, B: int, host_layers: dict, budget_s: float):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    """The CPU oracle, as it stands, on a bounded sample of the same workload.
+
+    Timed twice: with the BLAS library's own thread pool (every core this process may run on),
+    then limited to one thread, each on about half of `budget_s`.
+    """
     import numpy as np
     import oracle
     from synth import make_tokens
     try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:  # pragma: no cover
-        blas_threads = len(os.sched_getaffinity(0))
-    done, elapsed = 0, 0.0
-    per_layer = budget_s / max(1, len(host_layers))
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    blas_threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1) if threadpool_info else None
     ntok = min(cfg.tokens // B, 256)
+    decoded = {}
     for l, layer in host_layers.items():
         # decode the stored weights once per layer, outside the timed region
-        weights = (oracle.dense_weights(layer.w_gate, layer.s_gate) if layer.gated else None,
-                   oracle.dense_weights(layer.w_up, layer.s_up), oracle.dense_weights(layer.w_down_t, layer.s_down))
-        x = make_tokens(cfg, l, ntok * B)
-        spent = 0.0
-        for t in range(ntok):
-            t0 = time.perf_counter()
-            oracle.forward(layer, x[t * B:(t + 1) * B], mode, weights=weights)
-            spent += time.perf_counter() - t0
-            done += 1
-            if spent > per_layer:
-                break
-        elapsed += spent
-        del weights
-    return {"value": done / elapsed if elapsed > 0 else None, "unit": "layers/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"{done} layer-steps (batch {B}, {mode}) on layers {sorted(host_layers)}; float64 numpy, "
-                      f"weights decoded outside the timed region; {elapsed:.1f} s"}
+        decoded[l] = (oracle.dense_weights(layer.w_gate, layer.s_gate) if layer.gated else None,
+                      oracle.dense_weights(layer.w_up, layer.s_up),
+                      oracle.dense_weights(layer.w_down_t, layer.s_down))
+
+    def run(budget):
+        done, elapsed = 0, 0.0
+        per_layer = budget / max(1, len(host_layers))
+        for l, layer in host_layers.items():
+            x = make_tokens(cfg, l, ntok * B)
+            spent = 0.0
+            for t in range(ntok):
+                t0 = time.perf_counter()
+                oracle.forward(layer, x[t * B:(t + 1) * B], mode, weights=decoded[l])
+                spent += time.perf_counter() - t0
+                done += 1
+                if spent > per_layer:
+                    break
+            elapsed += spent
+        return done, elapsed
+
+    done, elapsed = run(0.5 * budget_s)
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, e1 = run(0.5 * budget_s)
+        single = d1 / e1 if e1 > 0 else None
+    return {"value": done / elapsed if elapsed > 0 else None, "unit": "layers/s", "cores": cores,
+            "blas_threads": blas_threads, "single_core_value": single, "kind": "oracle",
+            "sample": f"{done} layer-steps (batch {B}, {mode}) on layers {sorted(host_layers)} in {elapsed:.1f} s; "
+                      f"float64 numpy, weights decoded outside the timed region; single_core_value: the same "
+                      f"with BLAS limited to one thread"}
 
 
 def main() -> int:
@@ -268,7 +293,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256, help="timed steps (one step = one token through all layers)")
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--config", default="llama7b")
+    ap.add_argument("--config", default="llama70b",
+                    help="workload (default: the largest single-GPU one, Llama2-70B-ReLU-shaped, 80 layers)")
     ap.add_argument("--mode", default="predicted", choices=("predicted", "exact", "dense"))
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--tokens", type=int, default=64, help="distinct token inputs per layer, replayed round-robin")
@@ -276,6 +302,7 @@ def main() -> int:
     ap.add_argument("--rank", type=int, default=0,
                     help="override the predictor rank r (0 = the workload's own); for rank sweeps")
     ap.add_argument("--profile-tokens", type=int, default=4, help="tokens of the per-kernel event pass")
+    ap.add_argument("--repeats", type=int, default=5, help="further timed regions of --steps steps, for the spread")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -380,6 +407,17 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
     print(f"[bench] timed {args.steps} steps: {ms:.2f} ms", file=sys.stderr, flush=True)
+    # the same timed region repeated, for the spread between runs (the headline is the first)
+    repeats = []
+    for _ in range(args.repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(args.steps):
+            graphs[k % T].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        repeats.append(e0.elapsed_time(e1) / args.steps)
 
     cnt = counts.cpu().numpy().astype(np.int64)          # [T][L], deterministic per (token, layer)
     bytes_per_token = np.array([sum(step_bytes(cfg, mode, B, int(cnt[t, l])) for l in range(L)) for t in range(T)])
@@ -458,6 +496,8 @@ def main() -> int:
         "ffn_tokens_per_s": round(layers_per_s * B / L, 1),
         "alg_bytes_per_layer_step": round(total_bytes / (args.steps * L)),
         "us_per_layer_step": round(1e6 * sec / (L * args.steps), 3),
+        "repeat_ms_per_step": [round(v, 4) for v in repeats],
+        "median_layers_per_s": round(L / (1e-3 * float(np.median(repeats))), 1) if repeats else None,
         "kernel_sum_us_per_layer_step": round(sum_kernels_us, 3),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in phase_stats.items()},

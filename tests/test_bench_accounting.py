@@ -50,22 +50,28 @@ def test_expected_active_counts(name, B, count):
     assert abs(e - count) <= max(1.0, 2e-3 * count), f"{name} B={B}: E|M| = {e:.1f}, expected about {count}"
 
 
-@pytest.mark.parametrize("name,mode,B", [("llama7b", "predicted", 1), ("falcon40b", "predicted", 1),
-                                         ("llama70b", "predicted", 16), ("llama7b", "exact", 1)])
-def test_phase_bytes_cover_the_step(name, mode, B):
+@pytest.mark.parametrize("name,mode,B,path", [
+    ("llama7b", "predicted", 1, "split"), ("falcon40b", "predicted", 1, "split"), ("llama7b", "exact", 1, "split"),
+    ("llama70b", "dense", 1, "split"), ("llama70b", "predicted", 16, "batched"), ("llama7b", "exact", 4, "batched"),
+    ("toy", "predicted", 1, "vector"), ("toy", "exact", 1, "vector")])
+def test_phase_bytes_cover_the_step(name, mode, B, path):
     """The per-kernel algorithmic bytes (the roofline's numerator) add up to the step's bytes
     plus exactly the hand-offs between kernels: x read by a second kernel, h written and read
-    back (predicted mode), and the mask bits written (and read by the down kernel of a batch)."""
+    back (predicted mode), and the mask bits written and read again (by the down kernel of a
+    batch or of the one-token split path, or by the finish kernel)."""
     cfg = config_by_name(name)
-    count = 2000
-    phases = ("pred_hidden", "group", "finish") if mode == "predicted" else ("group", "finish")
-    if B > 1:
-        phases = phases[:-1] + ("down", "finish")
+    count = 2000 if mode != "dense" else cfg.d_ffn
+    head = ("pred_hidden",) if mode == "predicted" else ()
+    phases = head + {"split": ("group", "down"), "batched": ("group", "down", "finish"),
+                     "vector": ("group", "finish")}[path]
     total = sum(bench.phase_bytes(cfg, mode, ph, B, count, phases) for ph in phases)
     step = bench.step_bytes(cfg, mode, B, count)
-    handoff = cfg.d_ffn / 8 * (2 if B > 1 else 1)
+    if mode == "dense":
+        handoff = 0.0 if path == "split" else cfg.d_ffn / 8
+    else:
+        handoff = cfg.d_ffn / 8 * (2 if path != "vector" else 1)
     if mode == "predicted":
-        handoff += B * cfg.d_model * 2 + 2 * B * cfg.rank * 4
+        handoff += B * cfg.d_model * bench.esize(cfg.act_dtype) + 2 * B * cfg.rank * 4
     assert abs(total - (step + handoff)) <= 1, (total, step, handoff)
 
 
@@ -78,7 +84,7 @@ def test_counter_calibration_uses_only_the_calibration_copy(tmp_path):
             for name, value in rows:
                 f.write(f'"{name}",{counter},{value}\n')
 
-    copy, kern = "__amd_rocclr_copyBuffer", "void pik::k_ffn_wave<8>(pik::GroupArgs, int)"
+    copy, kern = "__amd_rocclr_copyBuffer", "void pik::k_act<1, 16, 0, 8>(pik::GroupArgs, float*)"
     fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
     # calibration copy: FETCH_SIZE reads half of 256 MiB, WRITE_SIZE all of it (KiB); a 1 GiB copy
     # reads four times as much; the kernel fetched 1000 KiB and wrote 10 KiB per dispatch

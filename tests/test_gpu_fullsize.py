@@ -8,9 +8,9 @@ and mode:
 * the index list must be the GPU's own decisions, bit-exact (checked through the logits);
 * every GPU logit (or, in exact mode, decision value) must lie within the rigorous fp32 error
   bound of the exact value, and within the much tighter probabilistic bound;
-* the list must agree with the oracle for every neuron outside twice the probabilistic band,
-  and the neurons inside it (either decision is correct there) are counted, reported and capped
-  at 1 % of the decisions;
+* the list must agree with the oracle for every neuron outside twice the probabilistic band;
+  the per-token decisions inside it (either decision is correct there) are counted, reported
+  and capped at 1 %, and the batch-union decisions they leave open are reported;
 * y must lie within rel-L2 1e-3 of the oracle evaluated on the GPU's index list.
 """
 
@@ -51,18 +51,24 @@ def _upload(name, layer_idx):
 
 
 class InBand:
-    """Counts the decisions inside the doubled probabilistic band."""
+    """Counts the per-token decisions inside the doubled probabilistic band (capped), and the
+    batch-union decisions left open by them (reported: with B tokens a neuron's union is open
+    when any token is in the band and none is certainly on)."""
 
     def __init__(self, what):
-        self.what, self.inside, self.total = what, 0, 0
+        self.what, self.inside, self.total, self.union_open, self.union_total = what, 0, 0, 0, 0
 
-    def add(self, inside, total):
-        self.inside += inside
-        self.total += total
+    def add(self, values, band, threshold, union_open):
+        v = np.atleast_2d(values)
+        self.inside += int(np.count_nonzero(np.abs(v - threshold) <= np.atleast_2d(band)))
+        self.total += v.size
+        self.union_open += union_open
+        self.union_total += v.shape[1]
 
     def close(self):
         frac = self.inside / max(1, self.total)
-        announce(f"  {self.what}: {self.inside} of {self.total} decisions inside the band ({100 * frac:.3f} %)")
+        announce(f"  {self.what}: {self.inside} of {self.total} token decisions inside the band ({100 * frac:.3f} %); "
+                 f"{self.union_open} of {self.union_total} union decisions open")
         assert frac <= IN_BAND_CAP, f"{self.what}: {frac:.4%} of decisions inside the band"
 
 
@@ -84,7 +90,8 @@ def _check_predicted(h, layer, cfg, B, n_batches, start0):
         prob = oracle.prob_band_predictor(x, layer.p1, layer.p2, layer.b_p)
         assert np.all(err <= rig), "logit outside the rigorous fp32 bound"
         assert np.all(err <= prob), f"logit outside the probabilistic bound (worst {np.max(err / prob):.3g} of it)"
-        counter.add(check_decisions(idx, layer.d_ffn, zo, oracle.GUARD_SAFETY * prob, thr), layer.d_ffn)
+        band = oracle.GUARD_SAFETY * prob
+        counter.add(zo, band, thr, check_decisions(idx, layer.d_ffn, zo, band, thr))
         ref = oracle.forward_masked(layer, x, idx)["y64"]
         err_y = rel_l2_rows(y, ref)
         assert err_y.max() <= 1e-3, err_y
@@ -106,7 +113,8 @@ def _check_exact(h, layer, cfg, B, n_batches, start0, pre):
         check_idx_valid(idx, count, layer.d_ffn)
         g = x.astype(np.float64) @ pre.T + layer.b
         prob = oracle.prob_band_exact(x, pre, layer.b)
-        counter.add(check_decisions(idx, layer.d_ffn, g, oracle.GUARD_SAFETY * prob, 0.0), layer.d_ffn)
+        band = oracle.GUARD_SAFETY * prob
+        counter.add(g, band, 0.0, check_decisions(idx, layer.d_ffn, g, band, 0.0))
         ref = oracle.forward_masked(layer, x, idx)["y64"]
         assert rel_l2_rows(y, ref).max() <= 1e-3
     counter.close()

@@ -1,14 +1,13 @@
-"""GPU parity of the wave-independent one-token predicted kernels (fp16
-activations and predictor, batch 1) against the CPU oracle: one wave per neuron
-for fp16 rows with d a multiple of 512 up to 4096; a wave pair per neuron (each
-wave half of d and of r, r <= 1024) for fp16 rows with d a multiple of 1024 from
-5120 to 8192 and for int4 group-32 rows with d = 4096 or 8192.
+"""GPU parity of the one-token split path (fp16 activations and predictor; fp16 rows with d a
+multiple of 512 up to 8192, int4 group-32 rows with d = 2048, 4096, 6144 or 8192) against the
+CPU oracle.  The path is k_act (each wave: its neurons' mask source, decisions, mask bits, and
+the gate / up rows of the selected ones) and k_down (column slice x list chunk tiles over the
+global list, the last tile of a slice adding the chunks' partials into y).
 
-Integer-lattice layers make every sum exact, so the index list, the logits and
-y must match the oracle bit for bit.  Shapes cover workgroups of one 8-neuron
-unit (small n), of 5-6 units (n spread over 256 workgroups) and of the
-64-neuron maximum (n large enough that 256 workgroups would not suffice), and
-d from 512 to 4096 including a non-power-of-two multiple of 512.
+Integer-lattice layers make every sum exact, so the index list, the logits and y must match the
+oracle bit for bit.  Shapes cover ragged neuron counts (a partly used last mask word), every
+mode (predicted, exact, dense, a caller's list), list chunks longer than one LDS segment,
+workspaces shared between layers of different sizes, and graph replay.
 """
 
 import numpy as np
@@ -17,7 +16,8 @@ import pytest
 import oracle
 from synth import config_by_name, make_lattice_layer, make_lattice_tokens, make_layer, make_tokens
 
-from gpu_util import announce, check_decisions, check_idx_valid, rel_l2_rows, run_forward, run_predict
+from gpu_util import (announce, check_decisions, check_idx_valid, rel_l2_rows, run_forward, run_masked,
+                      run_predict)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,13 +41,15 @@ def _bitwise(a, b):
 
 
 @pytest.mark.parametrize("d,n,r,gated", [
-    (512, 1000, 128, True),      # 125 units: one unit per workgroup, ragged last unit
-    (1536, 11000, 256, False),   # 1375 units over 256 workgroups (5-6 units each)
+    (512, 1000, 128, True),      # one slice, 64 chunks; a ragged last mask word
+    (1536, 11000, 256, False),   # three slices
     (4096, 11008, 1024, True),   # the LLaMA-7B shape
-    (2048, 20000, 64, True),     # 2500 units: 313 workgroups of 7-8 units (64 neurons)
+    (2048, 20000, 64, True),
+    (512, 1, 64, True),          # a single neuron
+    (1024, 37, 64, False),       # fewer neurons than one mask word
 ])
-def test_lattice_bit_exact_wave(d, n, r, gated):
-    announce(f"wave kernel lattice d={d} n={n} r={r} gated={gated}")
+def test_lattice_bit_exact_split(d, n, r, gated):
+    announce(f"split path lattice d={d} n={n} r={r} gated={gated}")
     layer = make_lattice_layer(d, n, r, gated, seed=d + n)
     h = _pi().upload_layer(layer, "cuda", max_batch=1)
     for t in range(3):
@@ -64,15 +66,15 @@ def test_lattice_bit_exact_wave(d, n, r, gated):
 
 
 @pytest.mark.parametrize("d,n,r,gated", [
-    (5120, 1000, 128, True),     # one unit per workgroup: pairs of 2 neurons, two pairs idle
-    (6144, 11000, 512, False),   # 5-6 units per workgroup
+    (5120, 1000, 128, True),
+    (6144, 11000, 512, False),
     (7168, 3000, 1024, False),   # the OPT-30B width and predictor rank
-    (8192, 20000, 256, True),    # 9-10 units per workgroup: 18-20 neurons per pair, mask bits across words
-    (5120, 40000, 128, False),   # 15-16 units per workgroup: up to 32 neurons per pair
-    (5120, 1000, 2048, True),    # r above 1024: the vector path
+    (8192, 20000, 256, True),
+    (5120, 40000, 128, False),
+    (5120, 1000, 2048, True),    # a predictor rank above 1024
 ])
-def test_lattice_bit_exact_wave_pairs(d, n, r, gated):
-    announce(f"wave-pair kernel lattice d={d} n={n} r={r} gated={gated}")
+def test_lattice_bit_exact_split_wide(d, n, r, gated):
+    announce(f"split path lattice d={d} n={n} r={r} gated={gated}")
     layer = make_lattice_layer(d, n, r, gated, seed=d + n + r)
     h = _pi().upload_layer(layer, "cuda", max_batch=1)
     for t in range(2):
@@ -89,15 +91,16 @@ def test_lattice_bit_exact_wave_pairs(d, n, r, gated):
 
 
 @pytest.mark.parametrize("d,n,r,gated", [
-    (4096, 3000, 128, True),     # gated int4, one chunk per lane of each half row
-    (8192, 5000, 256, False),    # the Falcon-40B width, 2-3 units per workgroup
-    (8192, 33000, 1024, False),  # 16 units per workgroup: 32 neurons per pair, several steps per pair
+    (4096, 3000, 128, True),     # gated int4
+    (8192, 5000, 256, False),    # the Falcon-40B width
+    (8192, 33000, 1024, False),
+    (2048, 1000, 64, True),      # one int4 chunk per lane
 ])
-def test_lattice_bit_exact_wave_pairs_int4(d, n, r, gated):
-    announce(f"wave-pair kernel int4 lattice d={d} n={n} r={r} gated={gated}")
+def test_lattice_bit_exact_split_int4(d, n, r, gated):
+    announce(f"split path int4 lattice d={d} n={n} r={r} gated={gated}")
     layer = make_lattice_layer(d, n, r, gated, w_dtype="q4g32", seed=d + n + r + 1)
     h = _pi().upload_layer(layer, "cuda", max_batch=1)
-    assert h.launch_plan(1, "predicted") == ("pred_hidden", "group", "finish")
+    assert h.launch_plan(1, "predicted") == ("pred_hidden", "group", "down")
     for t in range(2):
         x = make_lattice_tokens(d, 1, seed=70 + t)
         ref = oracle.forward(layer, x, "predicted")
@@ -111,9 +114,9 @@ def test_lattice_bit_exact_wave_pairs_int4(d, n, r, gated):
     h.close()
 
 
-def test_lattice_wave_pairs_nothing_selected():
+def test_lattice_split_wide_nothing_selected():
     d, n, r = 8192, 3000, 256
-    announce("wave-pair kernel: no neuron selected")
+    announce("split path d=8192: no neuron selected")
     layer = make_lattice_layer(d, n, r, False, seed=79)
     layer.b_p = np.full(n, -1000.0, dtype=np.float32)
     h = _pi().upload_layer(layer, "cuda", max_batch=1)
@@ -123,10 +126,10 @@ def test_lattice_wave_pairs_nothing_selected():
     h.close()
 
 
-def test_lattice_wave_nothing_selected():
+def test_lattice_split_nothing_selected():
     """Every logit below the threshold: the list is empty and y is +0.0."""
     d, n, r = 1024, 3000, 128
-    announce("wave kernel: no neuron selected")
+    announce("split path d=1024: no neuron selected")
     layer = make_lattice_layer(d, n, r, True, seed=77)
     layer.b_p = np.full(n, -1000.0, dtype=np.float32)
     h = _pi().upload_layer(layer, "cuda", max_batch=1)
@@ -137,9 +140,9 @@ def test_lattice_wave_nothing_selected():
     h.close()
 
 
-def test_random_llama7b_layer_wave_and_graph_replay():
+def test_random_llama7b_layer_split_and_graph_replay():
     cfg = config_by_name("llama7b")
-    announce("wave kernel: random LLaMA-7B layer, guard-band parity and graph replay")
+    announce("split path: random LLaMA-7B layer, guard-band parity and graph replay")
     layer = make_layer(cfg, 3)
     pi = _pi()
     h = pi.upload_layer(layer, "cuda", max_batch=1)
@@ -171,7 +174,7 @@ def test_random_llama7b_layer_wave_and_graph_replay():
         torch.cuda.synchronize()
         assert _bitwise(yt.cpu().numpy(), y), f"replay {rep}"
         assert int(ct.item()) == count and np.array_equal(it[:count].cpu().numpy(), idx)
-        h.forward(xt, yt, "exact")   # eager work (the vector kernel) between replays
+        h.forward(xt, yt, "exact")   # eager work between replays
         torch.cuda.synchronize()
     h.close()
 
@@ -181,10 +184,15 @@ def test_launch_plan_reports_the_kernels():
     announce("launch plans of the one-token, batched and vector paths")
     big = make_lattice_layer(4096, 11008, 1024, True, seed=1)
     h = pi.upload_layer(big, "cuda", max_batch=16)
-    assert h.launch_plan(1, "predicted") == ("pred_hidden", "group", "finish")
+    assert h.launch_plan(1, "predicted") == ("pred_hidden", "group", "down")
+    assert h.launch_plan(1, "exact") == ("group", "down")
+    assert h.launch_plan(1, "dense") == ("group", "down")
     assert h.launch_plan(4, "predicted") == ("pred_hidden", "group", "down", "finish")
-    assert h.launch_plan(1, "exact") == ("group", "finish")
     assert h.launch_plan(16, "dense") == ("group", "down", "finish")
+    h.close()
+    odd = make_lattice_layer(576, 1000, 128, True, seed=2)      # d not a multiple of 512: the vector path
+    h = pi.upload_layer(odd, "cuda", max_batch=1)
+    assert h.launch_plan(1, "predicted") == ("pred_hidden", "group", "finish")
     h.close()
 
 
@@ -215,3 +223,54 @@ def test_shared_workspace_smaller_layer_after_larger(d, w_dtype):
         run_forward(hb, xb, "predicted")                   # the larger layer again, in between
     hs.close()
     hb.close()
+
+
+@pytest.mark.parametrize("d,n,w_dtype,gated", [
+    (512, 1000, "f16", True), (4096, 11008, "f16", False), (8192, 3000, "f16", True),
+    (4096, 3000, "q4g32", False), (8192, 2000, "q4g32", True),
+])
+@pytest.mark.parametrize("mode", ["exact", "dense"])
+def test_lattice_split_exact_and_dense(d, n, w_dtype, gated, mode):
+    announce(f"split path lattice {mode} d={d} n={n} {w_dtype} gated={gated}")
+    layer = make_lattice_layer(d, n, 64, gated, w_dtype=w_dtype, seed=d + n + 5)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    assert h.launch_plan(1, mode) == ("group", "down")
+    for t in range(2):
+        x = make_lattice_tokens(d, 1, seed=120 + t)
+        ref = oracle.forward(layer, x, mode)
+        idx, count, y = run_forward(h, x, mode)
+        check_idx_valid(idx, count, n)
+        assert count == ref["count"] and np.array_equal(idx, ref["idx"]), f"token {t}"
+        assert _bitwise(y, ref["y"]), f"token {t}: y differs bitwise"
+    h.close()
+
+
+@pytest.mark.parametrize("d,n,w_dtype", [(512, 3000, "f16"), (8192, 5000, "f16"), (8192, 4000, "q4g32")])
+def test_lattice_split_forward_masked(d, n, w_dtype):
+    announce(f"split path forward_masked d={d} n={n} {w_dtype}")
+    layer = make_lattice_layer(d, n, 64, True, w_dtype=w_dtype, seed=d + n + 6)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    x = make_lattice_tokens(d, 1, seed=130)
+    rng = np.random.default_rng(131)
+    for sel in ([], [0], [n - 1], sorted(rng.choice(n, n // 7, replace=False).tolist()), list(range(n))):
+        y = run_masked(h, x, sel)
+        ref = oracle.forward_masked(layer, x, sel)["y"]
+        assert _bitwise(y, ref), f"list of {len(sel)}"
+        if not sel:
+            assert not np.signbit(y).any(), "an empty list must write +0.0"
+    h.close()
+
+
+def test_lattice_split_long_chunks():
+    """Dense mode on a narrow, very wide layer: every list chunk spans several LDS segments."""
+    d, n = 512, 150000      # one slice, 64 chunks of ~2344 neurons
+    announce(f"split path dense d={d} n={n}: chunks over several segments")
+    layer = make_lattice_layer(d, n, 64, False, seed=140, w_nonzero=0.05, down_nonzero=1 / 256)
+    h = _pi().upload_layer(layer, "cuda", max_batch=1)
+    x = make_lattice_tokens(d, 1, seed=141)
+    for mode in ("dense", "exact"):
+        ref = oracle.forward(layer, x, mode)
+        idx, count, y = run_forward(h, x, mode)
+        assert count == ref["count"] and np.array_equal(idx, ref["idx"]), mode
+        assert _bitwise(y, ref["y"]), mode
+    h.close()
