@@ -34,11 +34,12 @@
 
 namespace pik {
 
-// Exclusive prefix sum over the workgroup; *total gets the sum of all values.
+// Exclusive prefix sum over a workgroup of NT threads; *total gets the sum of all values.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
-  __shared__ int s_wave[16];
+  __shared__ int s_wave[NT / WAVE];
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int nwaves = blockDim.x / WAVE;
+  const int nwaves = NT / WAVE;
   int incl = v;
 #pragma unroll
   for (int off = 1; off < WAVE; off <<= 1) {
@@ -71,15 +72,16 @@ __device__ __forceinline__ unsigned mask_word(const unsigned* words, int w, int 
 // count, by one workgroup.  Each thread owns a contiguous run of words; a scan
 // of the per-thread popcounts gives every thread its output offset, so the
 // list comes out in order.
+template <int NT>
 __device__ inline void block_compact(const unsigned* words, int n, int* idx, int* count) {
-  const int T = blockDim.x, tid = threadIdx.x;
+  const int T = NT, tid = threadIdx.x;
   const int n_words = (n + 31) / 32;
   const int wpt = (n_words + T - 1) / T;
   const int w0 = min(tid * wpt, n_words), w1 = min(w0 + wpt, n_words);
   int c = 0;
   for (int w = w0; w < w1; ++w) c += __popc(mask_word(words, w, n));
   int total;
-  int pos = block_exclusive_scan(c, &total);
+  int pos = block_exclusive_scan<NT>(c, &total);
   for (int w = w0; w < w1; ++w) {
     unsigned m = mask_word(words, w, n);
     while (m) {
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(256) void k_finish(const float* __restrict__ partia
   if ((int)blockIdx.x == n_col_blocks) {
     if (blockIdx.y != 0) return;
     if (mask_words != nullptr) {
-      block_compact(mask_words, mask_n, idx_out, count_out);
+      block_compact<256>(mask_words, mask_n, idx_out, count_out);
     } else if (iota_n > 0) {
       for (int i = threadIdx.x; i < iota_n; i += blockDim.x) idx_out[i] = i;
       if (threadIdx.x == 0) *count_out = iota_n;

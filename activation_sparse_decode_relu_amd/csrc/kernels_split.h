@@ -31,8 +31,6 @@
 namespace pik {
 
 constexpr int kActWaves = 4;          // independent waves per k_act workgroup
-constexpr int kDnThreads = 256;       // 4 waves per k_down workgroup
-constexpr int kDnWaves = kDnThreads / WAVE;
 constexpr int kDnSeg = 1024;          // list entries of a chunk staged in LDS at a time
 constexpr int kCoherent = 16;         // buffer cache policy sc1: coherent across compute units
 constexpr int kRsrcFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
@@ -40,7 +38,9 @@ constexpr int kRsrcFlags = 0x00020000;   // buffer resource word 3: raw 32-bit d
 // ---------------------------------------------------------------------------------------------
 // k_act
 // ---------------------------------------------------------------------------------------------
-template <int WT, int CPL, int MODE, int NPW>
+// XLDS: the workgroup stages x in LDS once and the waves read their chunks from there at each
+// selected neuron, instead of each wave holding x in registers (64 VGPRs at d = 8192).
+template <int WT, int CPL, int MODE, int NPW, bool XLDS>
 __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, float* __restrict__ abuf) {
   constexpr int EPC = WFmt<WT>::EPC;
   static_assert(NPW == 8 || NPW == 16 || NPW == 32, "mask bits are written as whole bytes");
@@ -48,6 +48,13 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
   const int wid = blockIdx.x * kActWaves + (int)(threadIdx.x / WAVE);
   const int n = A.n, d = A.d;
   const int base = wid * NPW;
+  const f16* xb = static_cast<const f16*>(A.x);
+  constexpr int kXU = XLDS ? CPL * WAVE * EPC / 8 : 1;   // x as 16-byte units
+  __shared__ u32x4 s_x[kXU];
+  if constexpr (XLDS) {
+    for (int k = threadIdx.x; k < kXU; k += kActWaves * WAVE) s_x[k] = reinterpret_cast<const u32x4*>(xb)[k];
+    __syncthreads();
+  }
   int limit = n;   // neurons (or list entries) that exist
   if (MODE == MODE_LIST) limit = min(max(*A.list_count, 0), n);
   if (base >= limit) return;
@@ -71,7 +78,6 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
 
   const size_t rbytes = row_bytes(WT, d);
   const int spr = d / 32;   // int4 scales per row
-  const f16* xb = static_cast<const f16*>(A.x);
   const bool gated = A.gated != 0;
 
   // ---- decisions ------------------------------------------------------------------------------
@@ -128,10 +134,10 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
   // ---- activations of the selected neurons ------------------------------------------------------
   const bool need_gate = gated && MODE != MODE_EXACT;
   const bool need_up = gated || MODE != MODE_EXACT;   // exact, non-gated: a = ReLU(g) from the mask pass
-  XChunk<WT, DT_F16> xq[CPL];
-  if (need_gate || need_up) {
+  XChunk<WT, DT_F16> xq[XLDS ? 1 : CPL];
+  if (!XLDS && (need_gate || need_up)) {
 #pragma unroll
-    for (int q = 0; q < CPL; ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * EPC);
+    for (int q = 0; q < (XLDS ? 1 : CPL); ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * EPC);
   }
   const char* wgb = static_cast<const char*>(A.w_gate);
   const char* wub = static_cast<const char*>(A.w_up);
@@ -156,8 +162,11 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
     float pg = 0.f, pu = 0.f;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      if (need_gate) dot_chunk<WT, DT_F16>(pg, wg[q], xq[q], WT == DT_Q4 ? (float)rsg[q] : 1.f);
-      if (need_up) dot_chunk<WT, DT_F16>(pu, wu[q], xq[q], WT == DT_Q4 ? (float)rsu[q] : 1.f);
+      XChunk<WT, DT_F16> xl;
+      if constexpr (XLDS) xl.load(reinterpret_cast<const f16*>(s_x) + (size_t)(lane + q * WAVE) * EPC);
+      const XChunk<WT, DT_F16>& xc = XLDS ? xl : xq[XLDS ? 0 : q];
+      if (need_gate) dot_chunk<WT, DT_F16>(pg, wg[q], xc, WT == DT_Q4 ? (float)rsg[q] : 1.f);
+      if (need_up) dot_chunk<WT, DT_F16>(pu, wu[q], xc, WT == DT_Q4 ? (float)rsu[q] : 1.f);
     }
     const float gs = need_gate ? wave_sum(pg) : 0.f;
     const float us = need_up ? wave_sum(pu) : 0.f;
@@ -216,12 +225,17 @@ __device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, int byt
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
 }
 
-template <int WT, int MODE, int U>   // U: row pieces per wave per load batch
-__global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
+// NT: threads per tile.  LOCAL (mask modes): chunk c is the neurons of mask words
+// [c * words / C, (c + 1) * words / C) instead of positions [c * count / C, (c + 1) * count / C) of
+// the global list, so a tile reads and scans only its own words.
+template <int WT, int MODE, int U, int NT, bool LOCAL>
+__global__ __launch_bounds__(NT) void k_down(const DownArgs D) {
   using LD = DnLane<WT>;
   using V = typename LD::V;
   constexpr int EL = LD::EL;                    // columns per lane
   constexpr int SW = dn_slice_cols<WT>();       // columns per slice
+  constexpr int NWV = NT / WAVE;                // waves per tile
+  constexpr bool kMask = MODE == MODE_PRED || MODE == MODE_EXACT;
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int n = D.n, d = D.d, C = D.chunks;
   const int slice = blockIdx.x, chunk = blockIdx.y;
@@ -229,30 +243,30 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
   const bool col_ok = col < d;
 
   __shared__ int s_ids[kDnSeg];
-  __shared__ float s_red[kDnWaves][SW];
+  __shared__ float s_red[NWV][SW];
   __shared__ f32x4 s_half[SW / 4];
   __shared__ unsigned s_last;
 
-  // ---- the global list: count, and each thread's place in it (mask modes) ------------------------
+  // ---- tile (0, 0): the whole index list and count ------------------------------------------------
   const int n_words = (n + 31) / 32;
-  const int wpt = (n_words + kDnThreads - 1) / kDnThreads;
-  const int w0 = min((int)threadIdx.x * wpt, n_words), w1 = min(w0 + wpt, n_words);
-  int total = 0, my_pos = 0;
-  if (MODE == MODE_PRED || MODE == MODE_EXACT) {
+  const bool lister = slice == 0 && chunk == 0 && (D.idx_out != nullptr || D.count_out != nullptr);
+  int g_w0 = 0, g_w1 = 0, g_total = 0, g_pos = 0;   // the global scan: this thread's words and place
+  if (kMask && (lister || !LOCAL)) {
+    const int wpt = (n_words + NT - 1) / NT;
+    g_w0 = min((int)threadIdx.x * wpt, n_words);
+    g_w1 = min(g_w0 + wpt, n_words);
     int c = 0;
-    for (int w = w0; w < w1; ++w) c += __popc(mask_word(D.mask, w, n));
-    my_pos = block_exclusive_scan(c, &total);
+    for (int w = g_w0; w < g_w1; ++w) c += __popc(mask_word(D.mask, w, n));
+    g_pos = block_exclusive_scan<NT>(c, &g_total);
   } else if (MODE == MODE_DENSE) {
-    total = n;
-  } else {
-    total = min(max(*D.list_count, 0), n);
+    g_total = n;
+  } else if (MODE == MODE_LIST) {
+    g_total = min(max(*D.list_count, 0), n);
   }
-
-  // tile (0, 0) writes the index list and count
-  if (slice == 0 && chunk == 0) {
-    if (D.idx_out != nullptr && (MODE == MODE_PRED || MODE == MODE_EXACT)) {
-      int p = my_pos;
-      for (int w = w0; w < w1; ++w) {
+  if (lister) {
+    if (D.idx_out != nullptr && kMask) {
+      int p = g_pos;
+      for (int w = g_w0; w < g_w1; ++w) {
         unsigned mw = mask_word(D.mask, w, n);
         while (mw) {
           const int b = __ffs((int)mw) - 1;
@@ -261,14 +275,29 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
         }
       }
     } else if (D.idx_out != nullptr && MODE == MODE_DENSE) {
-      for (int i = threadIdx.x; i < n; i += kDnThreads) D.idx_out[i] = i;
+      for (int i = threadIdx.x; i < n; i += NT) D.idx_out[i] = i;
     }
-    if (D.count_out != nullptr && threadIdx.x == 0) *D.count_out = total;
+    if (D.count_out != nullptr && threadIdx.x == 0) *D.count_out = g_total;
   }
   if (!D.do_down) return;
 
-  // ---- this tile's chunk of the list, in segments staged in LDS ------------------------------------
-  const int lo = (int)((long long)chunk * total / C), hi = (int)((long long)(chunk + 1) * total / C);
+  // ---- this tile's chunk: [lo, hi) of the list, each thread's words and place in it ----------------
+  int w0 = g_w0, w1 = g_w1, my_pos = g_pos, lo, hi;
+  if (kMask && LOCAL) {
+    const int cw0 = (int)((long long)chunk * n_words / C), cw1 = (int)((long long)(chunk + 1) * n_words / C);
+    const int wpt = (cw1 - cw0 + NT - 1) / NT;
+    w0 = min(cw0 + (int)threadIdx.x * wpt, cw1);
+    w1 = min(w0 + wpt, cw1);
+    int c = 0;
+    for (int w = w0; w < w1; ++w) c += __popc(mask_word(D.mask, w, n));
+    int local;
+    my_pos = block_exclusive_scan<NT>(c, &local);
+    lo = 0;
+    hi = local;
+  } else {
+    lo = (int)((long long)chunk * g_total / C);
+    hi = (int)((long long)(chunk + 1) * g_total / C);
+  }
   const size_t rbytes = row_bytes(WT, d);
   const char* wdb = static_cast<const char*>(D.w_down_t) + row_bytes(WT, (size_t)(col_ok ? col : 0));
   const int spr = d / 32;
@@ -296,18 +325,18 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
         }
       }
     } else if (MODE == MODE_DENSE) {
-      for (int k = threadIdx.x; k < s1 - s0; k += kDnThreads) s_ids[k] = s0 + k;
+      for (int k = threadIdx.x; k < s1 - s0; k += NT) s_ids[k] = s0 + k;
     } else {
-      for (int k = threadIdx.x; k < s1 - s0; k += kDnThreads) {
+      for (int k = threadIdx.x; k < s1 - s0; k += NT) {
         const int id = D.list[s0 + k];
         s_ids[k] = ((unsigned)id < (unsigned)n) ? id : -1;
       }
     }
     __syncthreads();
-    // wave v takes entries v, v + 4, v + 8, ... of the segment, U at a time, two batches in flight:
-    // the next batch's row pieces are requested before the current batch is multiplied
+    // wave v takes entries v, v + NWV, v + 2 NWV, ... of the segment, U at a time, two batches in
+    // flight: the next batch's row pieces are requested before the current batch is multiplied
     const int cnt = s1 - s0;
-    const int mine = cnt > wave ? (cnt - wave + kDnWaves - 1) / kDnWaves : 0;   // this wave's entries
+    const int mine = cnt > wave ? (cnt - wave + NWV - 1) / NWV : 0;   // this wave's entries
     // a batch: U row pieces with their activations (one address for the whole wave) and int4 scales
     struct Batch {
       V w[U];
@@ -318,7 +347,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u;
-        const int id = i < mine ? s_ids[wave + kDnWaves * i] : -1;
+        const int id = i < mine ? s_ids[wave + NWV * i] : -1;
         const bool ok = id >= 0 && col_ok;
         bt.w[u] = ok ? ld_stream(reinterpret_cast<const V*>(wdb + rbytes * id)) : V{};
         bt.a[u] = id >= 0 ? D.abuf[id] : 0.f;
@@ -355,10 +384,10 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
   __syncthreads();
   const int ncol = min(SW, d - slice * SW);
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(D.partial, 0, 0x7fffffff, kRsrcFlags);
-  for (int q = threadIdx.x; q < ncol / 4; q += kDnThreads) {
+  for (int q = threadIdx.x; q < ncol / 4; q += NT) {
     f32x4 v = *reinterpret_cast<const f32x4*>(&s_red[0][4 * q]);
 #pragma unroll
-    for (int w = 1; w < kDnWaves; ++w) v += *reinterpret_cast<const f32x4*>(&s_red[w][4 * q]);
+    for (int w = 1; w < NWV; ++w) v += *reinterpret_cast<const f32x4*>(&s_red[w][4 * q]);
     store_coherent(prs, 4 * (chunk * d + slice * SW + 4 * q), v);
   }
 
@@ -375,8 +404,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
   if (s_last == 0u) return;
   // thread t: column quad t % Q of the slice, chunk group t / Q (chunks [g * per, (g + 1) * per));
   // every load of a group is issued before any is added; groups are then added in group order
-  constexpr int Q = SW / 4, H = kDnThreads / Q, kPer = kMaxDnChunks / H;
-  static_assert(H >= 1 && kDnThreads % Q == 0, "a slice's quads must divide the workgroup");
+  constexpr int Q = SW / 4, H = NT / Q, kPer = (kMaxDnChunks + H - 1) / H;
+  static_assert(H >= 1 && NT % Q == 0, "a slice's quads must divide the workgroup");
   const int quad = threadIdx.x % Q, grp = threadIdx.x / Q;
   const int per = (C + H - 1) / H, c0 = grp * per;
   const bool qok = 4 * quad < ncol;
@@ -389,12 +418,14 @@ __global__ __launch_bounds__(kDnThreads) void k_down(const DownArgs D) {
 #pragma unroll
   for (int u = 1; u < kPer; ++u)
     if (u < per && c0 + u < C) v += t[u];
-  if (H > 1) {
-    if (grp == 1) s_half[quad] = v;
+  // groups 1 .. H-1 hand their sums to group 0, which adds them in group order
+  for (int g = 1; g < H; ++g) {
+    if (grp == g) s_half[quad] = v;
+    __syncthreads();
+    if (grp == 0 && g * per < C) v += s_half[quad];
     __syncthreads();
   }
   if (grp == 0 && qok) {
-    if (H > 1 && per < C) v += s_half[quad];
     f16* yo = static_cast<f16*>(D.y) + (size_t)slice * SW + 4 * quad;
 #pragma unroll
     for (int e = 0; e < 4; ++e) yo[e] = (f16)v[e];

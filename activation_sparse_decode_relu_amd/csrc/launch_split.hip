@@ -7,7 +7,14 @@ namespace pik {
 
 namespace {
 
-constexpr int kNPW = 8;   // neurons per k_act wave: one mask byte
+// Chosen by timing the variants on Llama2-70B, LLaMA-7B and Falcon-40B int4 shaped layers (MI355X):
+constexpr int kNPW = 8;          // neurons per k_act wave: one mask byte (16 per wave: 4-25 % slower)
+constexpr bool kXLds = true;     // k_act: x staged in LDS (in registers: 1 % slower, more VGPRs)
+constexpr int kDnNT = 512;       // k_down: 8 waves per tile (4 waves: 6-35 % slower)
+constexpr int kDnTiles = 256;    // k_down: about one tile per compute unit
+// k_down chunks: fp16, each tile's own mask words (equal counts of the global list: 4-7 % slower);
+// int4, equal counts (3 % faster than own words)
+template <int WT> constexpr bool dn_local() { return WT == DT_F16; }
 
 int epc_of(int wt) { return wt == DT_Q4 ? 32 : (wt == DT_F16 ? 8 : 4); }
 
@@ -33,10 +40,10 @@ int split_slices(int wt, int d) {
 }
 
 int split_chunks(int wt, int d) {
-  // about 512 down tiles (two per compute unit), at most kMaxDnChunks partials per slice: the last
-  // tile of a slice reads them all in one round of loads
+  // about kDnTiles down tiles, at most kMaxDnChunks partials per slice: the last tile of a slice
+  // reads them all in one round of loads
   const int s = split_slices(wt, d);
-  return std::max(1, std::min(kMaxDnChunks, (512 + s - 1) / s));
+  return std::max(1, std::min(kMaxDnChunks, (kDnTiles + s - 1) / s));
 }
 
 template <int WT, int MODE>
@@ -45,7 +52,7 @@ static hipError_t act_cpl(const GroupArgs& a, float* abuf, int cpl, hipStream_t 
   const dim3 grid((waves + kActWaves - 1) / kActWaves), block(kActWaves * WAVE);
   switch (cpl) {
 #define PIK_ACT(C) \
-  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW>), grid, block, 0, s, a, abuf); break;
+  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW, kXLds>), grid, block, 0, s, a, abuf); break;
     PIK_ACT(1) PIK_ACT(2) PIK_ACT(3) PIK_ACT(4)
     default:
       if constexpr (WT == DT_F16) {
@@ -83,12 +90,12 @@ hipError_t launch_act(int wt, int mode, const GroupArgs& a, float* abuf, hipStre
 template <int WT>
 static hipError_t down_mode(int mode, const DownArgs& D, dim3 grid, hipStream_t s) {
   constexpr int U = WT == DT_Q4 ? 4 : 8;
-  const dim3 block(kDnThreads);
+  const dim3 block(kDnNT);
   switch (mode) {
-    case MODE_PRED: hipLaunchKernelGGL((k_down<WT, MODE_PRED, U>), grid, block, 0, s, D); break;
-    case MODE_EXACT: hipLaunchKernelGGL((k_down<WT, MODE_EXACT, U>), grid, block, 0, s, D); break;
-    case MODE_DENSE: hipLaunchKernelGGL((k_down<WT, MODE_DENSE, U>), grid, block, 0, s, D); break;
-    case MODE_LIST: hipLaunchKernelGGL((k_down<WT, MODE_LIST, U>), grid, block, 0, s, D); break;
+    case MODE_PRED: hipLaunchKernelGGL((k_down<WT, MODE_PRED, U, kDnNT, dn_local<WT>()>), grid, block, 0, s, D); break;
+    case MODE_EXACT: hipLaunchKernelGGL((k_down<WT, MODE_EXACT, U, kDnNT, dn_local<WT>()>), grid, block, 0, s, D); break;
+    case MODE_DENSE: hipLaunchKernelGGL((k_down<WT, MODE_DENSE, U, kDnNT, dn_local<WT>()>), grid, block, 0, s, D); break;
+    case MODE_LIST: hipLaunchKernelGGL((k_down<WT, MODE_LIST, U, kDnNT, dn_local<WT>()>), grid, block, 0, s, D); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
