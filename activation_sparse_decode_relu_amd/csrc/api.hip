@@ -89,7 +89,6 @@ Layout layout_for(const pi_ffn_desc& d) {
   // [chunks][d] on the split path
   L.max_partials = L.n_groups;
   if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
-  L.max_partials = std::max(L.max_partials, pik::wave_grid(d.d_ffn, d.d_model, d.w_dtype));
   const size_t split_part = (size_t)pik::split_chunks(d.w_dtype, d.d_model) * dm;
   L.partial = off; off = align_up(off + sizeof(float) * std::max((size_t)L.max_partials * B * dm, split_part));
   // the split path's ticket counter per column slice (zero between calls)

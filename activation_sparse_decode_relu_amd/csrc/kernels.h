@@ -51,15 +51,6 @@ int batch_down_chunks(int d);
 hipError_t launch_ffn_bgroup(int mode, const GroupArgs& a, float* abuf, hipStream_t s);
 hipError_t launch_ffn_bdown(int mode, const GroupArgs& a, const float* abuf, int chunks, hipStream_t s);
 
-// The wave-independent one-token predicted kernels (fp16 activations and predictor; fp16
-// weights with d = 512 .. 4096 in steps of 512 on single waves, or d = 5120 .. 8192 in steps of
-// 1024 on wave pairs; int4 weights with d = 4096 or 8192 on wave pairs; wave pairs need
-// r <= 1024): wave_grid(n, d, wt) workgroups, each writing one partial of y and whole bytes of
-// the mask.
-constexpr int kWaveGridBase = 256;   // one workgroup per compute unit of an MI355X
-bool wave_supported(int wt, int at, int pt, int mode, int B, int d, int r);
-int wave_grid(int n, int d, int wt);   // at most (n + 7) / 8, and at most wave_grid(n, 512, fp16)
-hipError_t launch_ffn_wave(int wt, const GroupArgs& a, hipStream_t s);
 
 // The one-token split path (fp16 activations, fp16 or int4 weights, fp16 predictor, batch 1):
 // k_act writes the mask bits and a[neuron] (fp32) into abuf; k_down sums a * W_down^T rows over
