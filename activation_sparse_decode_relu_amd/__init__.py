@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     check,
     last_error,
     make_desc,
+    probe_read,
     upload_layer,
     workspace_bytes,
 )

@@ -28,11 +28,11 @@ PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "group": PI_PHASE_GROUP, "down": 
           "finish": PI_PHASE_FINISH}
 STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_ERR_HIP", 4: "PI_ERR_UNSUPPORTED"}
 
-ABI_VERSION = 3   # PI_FFN_ABI_VERSION of the header this binding follows
+ABI_VERSION = 4   # PI_FFN_ABI_VERSION of the header this binding follows
 
 EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",
             "pi_ffn_destroy", "pi_ffn_predict", "pi_ffn_forward", "pi_ffn_forward_masked",
-            "pi_ffn_launch_plan", "pi_ffn_profile_next")
+            "pi_probe_read", "pi_ffn_launch_plan", "pi_ffn_profile_next")
 
 
 class PiDesc(ctypes.Structure):
@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.pi_ffn_forward.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
     lib.pi_ffn_forward_masked.restype = st
     lib.pi_ffn_forward_masked.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.pi_probe_read.restype = st
+    lib.pi_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
     lib.pi_ffn_launch_plan.restype = st
     lib.pi_ffn_launch_plan.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_uint32)]
     lib.pi_ffn_profile_next.restype = st
@@ -141,6 +143,7 @@ class FFNLayer:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         self.workspace = workspace
         w = PiWeights(*[_ptr(self.tensors.get(k)) for k, _ in PiWeights._fields_])
+        self.weights = w
         handle = ctypes.c_void_p()
         check(LIB.pi_ffn_create(ctypes.byref(desc), ctypes.byref(w), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream),
@@ -206,3 +209,10 @@ def upload_layer(layer, device="cuda", max_batch=1, workspace=None, stream=None,
     desc = make_desc(layer.d_model, layer.d_ffn, rank, layer.gated, max_batch, layer.w_dtype,
                      layer.p_dtype, layer.act_dtype, layer.tau)
     return FFNLayer(desc, tensors, workspace=workspace, stream=stream)
+
+
+def probe_read(buf, sums, stream=None) -> None:
+    """pi_probe_read: read every byte of the device tensor `buf` once; sums (uint32 device tensor)
+    receives one word-sum per workgroup."""
+    check(LIB.pi_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sums), int(sums.numel()),
+                            _stream(stream)))

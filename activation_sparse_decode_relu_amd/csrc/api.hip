@@ -78,6 +78,11 @@ Layout layout_for(const pi_ffn_desc& d) {
   L.n_groups = (d.d_ffn + L.group - 1) / L.group;
   L.n_words = (d.d_ffn + 31) / 32;
   size_t off = 0;
+  // The split path's ticket counters come first, at the same offset and size for every
+  // descriptor: handles of different shapes that share a workspace then share the tickets too,
+  // which every call leaves at zero, and no other region of another layout overlaps them.
+  L.slices = pik::split_slices(d.w_dtype, d.d_model);
+  L.tickets = off; off = align_up(off + sizeof(unsigned) * (size_t)pik::kMaxDnSlices * pik::kTicketStride);
   L.h = off;       off = align_up(off + sizeof(float) * B * (size_t)(d.rank > 0 ? d.rank : 1));
   L.mask = off;    off = align_up(off + sizeof(unsigned) * (size_t)L.n_words);
   L.idx = off;     off = align_up(off + sizeof(int) * n);
@@ -91,9 +96,6 @@ Layout layout_for(const pi_ffn_desc& d) {
   if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
   const size_t split_part = (size_t)pik::split_chunks(d.w_dtype, d.d_model) * dm;
   L.partial = off; off = align_up(off + sizeof(float) * std::max((size_t)L.max_partials * B * dm, split_part));
-  // the split path's ticket counter per column slice (zero between calls)
-  L.slices = pik::split_slices(d.w_dtype, d.d_model);
-  L.tickets = off; off = align_up(off + sizeof(unsigned) * (size_t)L.slices * pik::kTicketStride);
   L.total = off;
   return L;
 }
@@ -275,6 +277,9 @@ pi_status group_phase(pi_ffn* h, int mode, const Plan& plan, const pik::GroupArg
                    [&] { return pik::launch_ffn_group(d.w_dtype, d.act_dtype, mode, a, s); });
 }
 
+pi_status forward_impl(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
+                       int32_t* count_out, void* stream);
+
 // The one-token split path: act, then down (y, and the index list when idx / count are given).
 pi_status split_phases(pi_ffn* h, int mode, const pik::GroupArgs& a, void* y, int* idx, int* count, hipStream_t s) {
   const pi_ffn_desc& d = h->desc;
@@ -307,6 +312,51 @@ pi_status finish_phase(pi_ffn* h, int B, int partials, void* y, bool reduce, int
     return pik::launch_finish(d.act_dtype, h->partial(), partials, B, d.d_model, y, list == 1 ? h->mask() : nullptr,
                               d.d_ffn, list == 2 ? d.d_ffn : 0, idx, count, reduce, list != 0, s);
   });
+}
+
+// The whole step of pi_ffn_forward on a handle.
+pi_status forward_impl(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
+                       int32_t* count_out, void* stream) {
+  pi_status st = check_call(h, x, batch, y, true);
+  if (st != PI_OK) return st;
+  if ((st = check_int_ptr(idx_out, "idx_out")) != PI_OK || (st = check_int_ptr(count_out, "count_out")) != PI_OK)
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const pi_ffn_desc& d = h->desc;
+  const bool want_list = idx_out != nullptr || count_out != nullptr;
+  int* idx = idx_out != nullptr ? idx_out : h->idx();
+  int* count = count_out != nullptr ? count_out : h->count();
+  pik::GroupArgs a = group_args(h, x, batch);
+  int mode, list;
+  switch (mask_mode) {
+    case PI_MASK_PREDICTED:
+      if (d.rank == 0) return fail(PI_ERR_INVALID, "PREDICTED mode needs a predictor (rank > 0)");
+      mode = pik::MODE_PRED;
+      list = 1;
+      break;
+    case PI_MASK_EXACT_RELU:
+      mode = pik::MODE_EXACT;
+      a.thr = 0.0f;   // the ReLU support: g > 0, whatever the predictor's tau
+      list = 1;
+      break;
+    case PI_MASK_DENSE:
+      mode = pik::MODE_DENSE;
+      list = 2;
+      break;
+    default:
+      return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
+  }
+  int partials = 0;
+  const Plan plan = plan_for(h, mode, batch);
+  if (mode == pik::MODE_PRED && (st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
+  if (plan.split) {
+    if ((st = split_phases(h, mode, a, y, want_list ? idx : nullptr, want_list ? count : nullptr, s)) != PI_OK)
+      return st;
+    return ok();
+  }
+  if ((st = group_phase(h, mode, plan, a, s, &partials)) != PI_OK) return st;
+  if ((st = finish_phase(h, batch, partials, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
+  return ok();
 }
 
 }  // namespace
@@ -350,7 +400,7 @@ pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights, 
   // Clear the mask words once so a predict() before any forward() never reads garbage.
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pik::launch_fill_u32(h->mask(), L.n_words, 0u, s);
-  if (e == hipSuccess) e = pik::launch_fill_u32(h->tickets(), L.slices * pik::kTicketStride, 0u, s);
+  if (e == hipSuccess) e = pik::launch_fill_u32(h->tickets(), pik::kMaxDnSlices * pik::kTicketStride, 0u, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete h;
@@ -393,46 +443,7 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, 
 
 pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
                          int32_t* count_out, void* stream) {
-  pi_status st = check_call(h, x, batch, y, true);
-  if (st != PI_OK) return st;
-  if ((st = check_int_ptr(idx_out, "idx_out")) != PI_OK || (st = check_int_ptr(count_out, "count_out")) != PI_OK)
-    return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const pi_ffn_desc& d = h->desc;
-  const bool want_list = idx_out != nullptr || count_out != nullptr;
-  int* idx = idx_out != nullptr ? idx_out : h->idx();
-  int* count = count_out != nullptr ? count_out : h->count();
-  pik::GroupArgs a = group_args(h, x, batch);
-  int mode, list;
-  switch (mask_mode) {
-    case PI_MASK_PREDICTED:
-      if (d.rank == 0) return fail(PI_ERR_INVALID, "PREDICTED mode needs a predictor (rank > 0)");
-      mode = pik::MODE_PRED;
-      list = 1;
-      break;
-    case PI_MASK_EXACT_RELU:
-      mode = pik::MODE_EXACT;
-      a.thr = 0.0f;   // the ReLU support: g > 0, whatever the predictor's tau
-      list = 1;
-      break;
-    case PI_MASK_DENSE:
-      mode = pik::MODE_DENSE;
-      list = 2;
-      break;
-    default:
-      return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
-  }
-  int partials = 0;
-  const Plan plan = plan_for(h, mode, batch);
-  if (mode == pik::MODE_PRED && (st = hidden_phase(h, x, batch, s)) != PI_OK) return st;
-  if (plan.split) {
-    if ((st = split_phases(h, mode, a, y, want_list ? idx : nullptr, want_list ? count : nullptr, s)) != PI_OK)
-      return st;
-    return ok();
-  }
-  if ((st = group_phase(h, mode, plan, a, s, &partials)) != PI_OK) return st;
-  if ((st = finish_phase(h, batch, partials, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
-  return ok();
+  return forward_impl(h, x, batch, mask_mode, y, idx_out, count_out, stream);
 }
 
 pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx, const int32_t* count,
@@ -476,6 +487,15 @@ pi_status pi_ffn_launch_plan(const pi_ffn* h, int32_t batch, int32_t mask_mode, 
   if (mode == pik::MODE_PRED) bits |= 1u << PI_PHASE_PRED_HIDDEN;
   if (p.batched || p.split) bits |= 1u << PI_PHASE_DOWN;
   *plan = bits;
+  return ok();
+}
+
+pi_status pi_probe_read(const void* buf, size_t bytes, uint32_t* sums, int32_t n_sums, void* stream) {
+  if (buf == nullptr || sums == nullptr) return fail(PI_ERR_INVALID, "buf and sums are required");
+  if (!aligned16(buf) || bytes % 16 != 0) return fail(PI_ERR_INVALID, "buf must be 16-byte aligned and bytes a multiple of 16");
+  if (n_sums < 1 || n_sums > 65536) return fail(PI_ERR_INVALID, "n_sums=%d must lie in [1, 65536]", n_sums);
+  const hipError_t e = pik::launch_read_probe(buf, bytes / 16, sums, n_sums, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PI_ERR_HIP, "read probe launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -72,11 +72,16 @@ struct DownArgs {
 };
 constexpr int kMaxDnChunks = 32;   // list chunks per column slice (partials the last tile adds)
 constexpr int kTicketStride = 64;  // one ticket per 256 bytes: tickets of different slices share no line
+constexpr int kMaxDnSlices = 16;   // column slices of the split path's widest rows (fp16, d = 8192)
 bool split_supported(int wt, int at, int pt, int B, int d, int r);
 int split_slices(int wt, int d);
 int split_chunks(int wt, int d);
 hipError_t launch_act(int wt, int mode, const GroupArgs& a, float* abuf, hipStream_t s);
 hipError_t launch_down(int wt, int mode, const DownArgs& D, hipStream_t s);
+
+// Read-bandwidth probe: n16 16-byte units of buf, summed as 32-bit words (mod 2^32) into
+// sums[n_sums], one sum per workgroup.
+hipError_t launch_read_probe(const void* buf, size_t n16, unsigned* sums, int n_sums, hipStream_t s);
 
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
                          const unsigned* mask_words, int mask_n, int iota_n, int* idx_out, int* count_out,

@@ -57,6 +57,38 @@ hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStr
   return launch_ffn_group_q4(at, mode, a, cpl, s);
 }
 
+// Every 16-byte unit of the buffer read once with streaming loads, 8 in flight per lane; the
+// words are summed (mod 2^32) so the reads cannot be dropped and their total can be checked.
+__global__ __launch_bounds__(256) void k_read_probe(const u32x4* __restrict__ p, size_t n16,
+                                                     unsigned* __restrict__ sums) {
+  constexpr int kU = 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  unsigned acc = 0u;
+  for (size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n16; i0 += stride * kU) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t i = i0 + (size_t)u * stride;
+      v[u] = i < n16 ? ld_stream(p + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc += v[u].x + v[u].y + v[u].z + v[u].w;
+  }
+  __shared__ unsigned s_acc[256];
+  s_acc[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned t = 0u;
+    for (int k = 0; k < 256; ++k) t += s_acc[k];
+    sums[blockIdx.x] = t;
+  }
+}
+
+hipError_t launch_read_probe(const void* buf, size_t n16, unsigned* sums, int n_sums, hipStream_t s) {
+  hipLaunchKernelGGL(k_read_probe, dim3(n_sums), dim3(kBlock), 0, s, static_cast<const u32x4*>(buf), n16, sums);
+  return hipGetLastError();
+}
+
 hipError_t launch_finish(int ot, const float* partial, int ng, int B, int d, void* y,
                          const unsigned* mask_words, int mask_n, int iota_n, int* idx_out, int* count_out,
                          bool reduce, bool index_list, hipStream_t s) {

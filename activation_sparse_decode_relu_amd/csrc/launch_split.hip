@@ -26,17 +26,18 @@ int row_cpl(int wt, int d) {
 
 }  // namespace
 
-bool split_supported(int wt, int at, int pt, int B, int d, int r) {
-  if (B != 1 || at != DT_F16 || (r > 0 && pt != DT_F16)) return false;
-  const int cpl = row_cpl(wt, d);
-  if (wt == DT_F16) return cpl >= 1 && cpl <= 16;   // d = 512 .. 8192 in steps of 512
-  if (wt == DT_Q4) return cpl >= 1 && cpl <= 4;     // d = 2048 .. 8192 in steps of 2048
-  return false;
-}
-
 int split_slices(int wt, int d) {
   const int sw = wt == DT_Q4 ? dn_slice_cols<DT_Q4>() : dn_slice_cols<DT_F16>();
   return (d + sw - 1) / sw;
+}
+
+bool split_supported(int wt, int at, int pt, int B, int d, int r) {
+  if (B != 1 || at != DT_F16 || (r > 0 && pt != DT_F16)) return false;
+  const int cpl = row_cpl(wt, d);
+  bool ok = false;
+  if (wt == DT_F16) ok = cpl >= 1 && cpl <= 16;   // d = 512 .. 8192 in steps of 512
+  if (wt == DT_Q4) ok = cpl >= 1 && cpl <= 4;     // d = 2048 .. 8192 in steps of 2048
+  return ok && split_slices(wt, d) <= kMaxDnSlices;
 }
 
 int split_chunks(int wt, int d) {

@@ -192,6 +192,28 @@ def copy_ceiling(mib: int = 1024, reps: int = 10) -> float:
     return gbps
 
 
+def read_ceiling(mib: int = 2048, reps: int = 10) -> float:
+    """Practical HBM read rate on this GPU: the library's read probe (every 16-byte unit of a
+    `mib` MiB buffer read once with streaming loads), bytes / time.  Context for the roofline
+    fractions, which are always taken against the published 8 TB/s peak."""
+    import torch
+    import activation_sparse_decode_relu_amd as pi
+    n = mib << 20
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sums = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pi.probe_read(buf, sums)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pi.probe_read(buf, sums)
+    e1.record()
+    e1.synchronize()
+    gbps = float(n) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sums
+    return gbps
+
+
 def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, workload: str, steps: int) -> dict:
     """Per-launch HBM bytes of each kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files.
 
@@ -470,6 +492,7 @@ def main() -> int:
         cpu = cpu_baseline(cfg, mode, B, host_sample, args.cpu_seconds)
 
     copy_gbps = None if args.copy_calib else copy_ceiling()   # counter runs keep only their calibration copy
+    read_gbps = None if args.copy_calib else read_ceiling()
 
     replayed = sorted({k % T for k in range(args.steps)})   # tokens the timed region ran
     mean_count = float(cnt[replayed].mean())
@@ -493,6 +516,7 @@ def main() -> int:
         "effective_hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "hbm_copy_gbps": round(copy_gbps, 1) if copy_gbps else None,   # context: a plain 1 GiB device copy
+        "hbm_read_gbps": round(read_gbps, 1) if read_gbps else None,   # context: the read probe over 2 GiB
         "ffn_tokens_per_s": round(layers_per_s * B / L, 1),
         "alg_bytes_per_layer_step": round(total_bytes / (args.steps * L)),
         "us_per_layer_step": round(1e6 * sec / (L * args.steps), 3),

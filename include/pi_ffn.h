@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define PI_FFN_ABI_VERSION 3
+#define PI_FFN_ABI_VERSION 4
 
 typedef enum pi_status {
   PI_OK = 0,
@@ -81,12 +81,16 @@ typedef enum pi_mask_mode {
 /* Kernels a profiling event pair can bracket (pi_ffn_profile_next). */
 typedef enum pi_phase {
   PI_PHASE_PRED_HIDDEN = 0, /* h = ReLU(x P1^T)                                        */
-  PI_PHASE_GROUP = 1,       /* per neuron group: mask, row gather, ReLU(g)*u, and (one
-                               token, or dtypes the matrix-core path does not take) the
-                               group's partial y                                         */
-  PI_PHASE_DOWN = 2,        /* batched matrix-core path only: partial y over (neuron
-                               chunk, column slice) from the group kernel's activations  */
-  PI_PHASE_FINISH = 3,      /* fixed-order sum of the partials; index list              */
+  PI_PHASE_GROUP = 1,       /* the mask and the gate/up row gather with a = ReLU(g)*u:
+                               one token (fp16 activations, fp16 or int4 rows): k_act;
+                               2..16 tokens on the matrix cores: k_ffn_bgroup; otherwise
+                               k_ffn_group, which also forms each group's partial y     */
+  PI_PHASE_DOWN = 2,        /* the down projection over (column slice, neuron chunk)
+                               tiles from the activations: one token, k_down (which also
+                               sums the partials into y and writes the index list);
+                               matrix-core batches, k_ffn_bdown                          */
+  PI_PHASE_FINISH = 3,      /* fixed-order sum of the partials; index list (every path
+                               but the one-token k_act / k_down path)                    */
   PI_PHASE_COUNT = 4
 } pi_phase;
 
@@ -130,7 +134,9 @@ pi_status pi_ffn_workspace_bytes(const pi_ffn_desc* desc, size_t* bytes);
  * Validate the descriptor and weights, bind them and the workspace to a new
  * handle, and clear the workspace's counters with a kernel on `stream`,
  * waiting for it before returning.  `workspace` is device memory of at least
- * pi_ffn_workspace_bytes(desc) bytes, 256-byte aligned.
+ * pi_ffn_workspace_bytes(desc) bytes, 256-byte aligned.  The weights are one FFN layer
+ * (paper explainer, section "ニューロン活性化のべき乗則分布", FFN equation) plus its predictor
+ * (section "活性化予測器"), laid out as the conventions above state.
  */
 pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights,
                         void* workspace, size_t workspace_bytes, void* stream,
@@ -140,7 +146,10 @@ pi_status pi_ffn_create(const pi_ffn_desc* desc, const pi_ffn_weights* weights,
 pi_status pi_ffn_destroy(pi_ffn* h);
 
 /*
- * Predictor and compaction alone.  For x [B][d]:
+ * Predictor and compaction alone: the activation predictor of the paper explainer, section
+ * "活性化予測器" (sigmoid(x W_p + b_p) > tau, read as a rank-r two-layer ReLU MLP; sigmoid(z) > tau
+ * is tested as z > log(tau/(1-tau))), and the list of neurons it selects, which the same page's
+ * inference flow (section "GPU-CPUハイブリッドアーキテクチャ") computes next.  For x [B][d]:
  *   h = ReLU(x P1^T), z = h P2^T + b_p, selected_i = OR_t (z[t][i] > log(tau/(1-tau))),
  * and writes idx[0..count) = ascending selected neurons (capacity n), *count.
  * logits_dbg, if not NULL, receives z as f32 [B][n].  Requires rank > 0.
@@ -149,8 +158,11 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx,
                          int32_t* count, float* logits_dbg, void* stream);
 
 /*
- * The whole step: mask (per mask_mode), compaction, the gathered activation
- * a = ReLU(g) (.) u over the selected neurons only, and
+ * The whole step, the paper explainer's FFN equation (section "ニューロン活性化のべき乗則分布")
+ * computed only over the neurons a mask selects (section "GPU-CPUハイブリッドアーキテクチャ",
+ * inference flow; paper summary, "Methodology": neuron-aware sparse operators): mask (per
+ * mask_mode: the predictor of section "活性化予測器", the exact ReLU support, or every neuron),
+ * compaction, the gathered activation a = ReLU(g) (.) u over the selected neurons only, and
  * y[t] = sum over selected i of a[t][i] * W_downT[i], rounded once to act dtype.
  * idx_out (capacity n) and count_out, if not NULL, receive the index list.
  * With no neuron selected, y is +0.0.
@@ -159,13 +171,23 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
                          void* y, int32_t* idx_out, int32_t* count_out, void* stream);
 
 /*
- * The sparse operator on a caller-given list: idx[0..*count) must be strictly
- * ascending neuron ids in [0, n) (the list is read on the device; it is not
- * validated), 0 <= *count <= n.  Computes the same y as pi_ffn_forward for
- * that list.  count == 0 writes +0.0.
+ * The neuron-aware sparse operator alone (paper summary, "Methodology"; paper explainer, section
+ * "GPU-CPUハイブリッドアーキテクチャ", inference flow step 2) on a caller-given list: idx[0..*count)
+ * must be strictly ascending neuron ids in [0, n) (the list is read on the device and not
+ * validated; an entry outside [0, n) contributes nothing), 0 <= *count <= n.  Computes the same
+ * y as pi_ffn_forward for that list.  count == 0 writes +0.0.
  */
 pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx,
                                 const int32_t* count, void* y, void* stream);
+
+/*
+ * Measurement aid, not part of the FFN: reads `bytes` of device memory at buf once with
+ * streaming 16-byte loads and writes the sum (mod 2^32) of the 32-bit words each of n_sums
+ * workgroups read to sums[0..n_sums), so the reads cannot be dropped and their total can be
+ * checked.  Timing it gives the read bandwidth this GPU sustains.  buf 16-byte aligned, bytes a
+ * multiple of 16, 1 <= n_sums <= 65536.
+ */
+pi_status pi_probe_read(const void* buf, size_t bytes, uint32_t* sums, int32_t n_sums, void* stream);
 
 /*
  * Which kernels pi_ffn_forward(h, x, batch, mask_mode, ...) launches, for profiling and

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(pi.LIB, name), f"{name} is declared in pi_ffn.h but not exported"
     assert set(declared_functions()) == set(pi.EXPORTED)
-    assert pi.LIB.pi_ffn_abi_version() == 3
+    assert pi.LIB.pi_ffn_abi_version() == 4
 
 
 def test_struct_layouts_match_header():
@@ -121,3 +121,11 @@ def test_package_fails_loudly_without_library(tmp_path):
     res = subprocess.run([sys.executable, "-c", "import activation_sparse_decode_relu_amd"], cwd=ROOT, env=env,
                          capture_output=True, text=True)
     assert res.returncode != 0 and "ImportError" in res.stderr
+
+
+def test_probe_read_validates_on_the_host():
+    pi = _pi()
+    assert pi.LIB.pi_probe_read(None, 16, 0x1000, 1, None) == 1
+    assert pi.LIB.pi_probe_read(0x1008, 16, 0x1000, 1, None) == 1      # misaligned
+    assert pi.LIB.pi_probe_read(0x1000, 20, 0x1000, 1, None) == 1      # not whole 16-byte units
+    assert pi.LIB.pi_probe_read(0x1000, 16, 0x1000, 0, None) == 1
