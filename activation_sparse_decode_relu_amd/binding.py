@@ -28,11 +28,12 @@ PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "group": PI_PHASE_GROUP, "down": 
           "finish": PI_PHASE_FINISH}
 STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_ERR_HIP", 4: "PI_ERR_UNSUPPORTED"}
 
-ABI_VERSION = 4   # PI_FFN_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5   # PI_FFN_ABI_VERSION of the header this binding follows
+STATIC_SCRATCH_BYTES = 16 << 20   # PI_FFN_STATIC_SCRATCH_BYTES
 
 EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",
             "pi_ffn_destroy", "pi_ffn_predict", "pi_ffn_forward", "pi_ffn_forward_masked",
-            "pi_probe_read", "pi_ffn_launch_plan", "pi_ffn_profile_next")
+            "pi_ffn_forward_static", "pi_probe_read", "pi_ffn_launch_plan", "pi_ffn_profile_next")
 
 
 class PiDesc(ctypes.Structure):
@@ -75,6 +76,9 @@ def _load() -> ctypes.CDLL:
     lib.pi_ffn_forward.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
     lib.pi_ffn_forward_masked.restype = st
     lib.pi_ffn_forward_masked.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.pi_ffn_forward_static.restype = st
+    lib.pi_ffn_forward_static.argtypes = [ctypes.POINTER(PiDesc), ctypes.POINTER(PiWeights), vp, i32, i32, vp, vp, vp,
+                                          vp]
     lib.pi_probe_read.restype = st
     lib.pi_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
     lib.pi_ffn_launch_plan.restype = st
@@ -169,6 +173,14 @@ class FFNLayer:
         m = MODES[mode] if isinstance(mode, str) else int(mode)
         check(LIB.pi_ffn_forward(self.handle, _ptr(x), int(x.shape[0]), m, _ptr(y), _ptr(idx_out),
                                  _ptr(count_out), _stream(stream)))
+
+    def forward_static(self, x, y, mode="predicted", idx_out=None, count_out=None, stream=None) -> None:
+        """pi_ffn_forward_static with this layer's descriptor and weights (the handle's workspace
+        is not used: the call works in the library's static scratch array)."""
+        m = MODES[mode] if isinstance(mode, str) else int(mode)
+        check(LIB.pi_ffn_forward_static(ctypes.byref(self.desc), ctypes.byref(self.weights), _ptr(x),
+                                        int(x.shape[0]), m, _ptr(y), _ptr(idx_out), _ptr(count_out),
+                                        _stream(stream)))
 
     def forward_masked(self, x, idx, count, y, stream=None) -> None:
         check(LIB.pi_ffn_forward_masked(self.handle, _ptr(x), int(x.shape[0]), _ptr(idx), _ptr(count),

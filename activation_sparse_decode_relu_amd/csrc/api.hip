@@ -24,6 +24,11 @@
 #include "kernels.h"
 #include "pi_ffn.h"
 
+#include <mutex>
+
+// The workspace of pi_ffn_forward_static (see static_scratch below).
+static __device__ __align__(256) char scratch[PI_FFN_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -314,7 +319,7 @@ pi_status finish_phase(pi_ffn* h, int B, int partials, void* y, bool reduce, int
   });
 }
 
-// The whole step of pi_ffn_forward on a handle.
+// The whole step of pi_ffn_forward, on a handle (a caller's, or the static scratch's).
 pi_status forward_impl(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
                        int32_t* count_out, void* stream) {
   pi_status st = check_call(h, x, batch, y, true);
@@ -357,6 +362,32 @@ pi_status forward_impl(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mod
   if ((st = group_phase(h, mode, plan, a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, y, true, want_list ? list : 0, idx, count, s)) != PI_OK) return st;
   return ok();
+}
+
+// ---- the static scratch of pi_ffn_forward_static ----------------------------------------------------
+// One array per GPU, held until the process ends.  In host code `scratch` is only a host-side
+// stand-in for the symbol: its device address on the current GPU comes from hipGetSymbolAddress,
+// taken once per device and kept, and only that address is ever handed to a kernel.
+constexpr size_t kStaticScratchBytes = PI_FFN_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];
+
+pi_status static_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PI_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PI_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PI_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return PI_OK;
 }
 
 }  // namespace
@@ -444,6 +475,32 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, 
 pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
                          int32_t* count_out, void* stream) {
   return forward_impl(h, x, batch, mask_mode, y, idx_out, count_out, stream);
+}
+
+pi_status pi_ffn_forward_static(const pi_ffn_desc* desc, const pi_ffn_weights* weights, const void* x, int32_t batch,
+                                int32_t mask_mode, void* y, int32_t* idx_out, int32_t* count_out, void* stream) {
+  pi_status st = check_desc(desc);
+  if (st != PI_OK) return st;
+  if ((st = check_weights(desc, weights)) != PI_OK) return st;
+  const Layout L = layout_for(*desc);
+  if (L.total > kStaticScratchBytes)
+    return fail(PI_ERR_WORKSPACE, "this descriptor needs %zu bytes of workspace; the static scratch holds %zu",
+                L.total, kStaticScratchBytes);
+  char* ws = nullptr;
+  if ((st = static_scratch(&ws)) != PI_OK) return st;
+  pi_ffn h{};   // on the stack: this call allocates nothing
+  h.desc = *desc;
+  h.w = *weights;
+  h.ws = ws;
+  h.ws_bytes = kStaticScratchBytes;
+  h.L = L;
+  h.thr = desc->rank > 0 ? (float)std::log((double)desc->tau / (1.0 - (double)desc->tau)) : 0.0f;
+  if ((st = check_call(&h, x, batch, y, true)) != PI_OK) return st;
+  // the split path's tickets must be zero; the scratch's last user may have laid it out differently
+  const hipError_t e =
+      pik::launch_fill_u32(h.tickets(), pik::kMaxDnSlices * pik::kTicketStride, 0u, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PI_ERR_HIP, "clearing the static scratch's tickets failed: %s", hipGetErrorString(e));
+  return forward_impl(&h, x, batch, mask_mode, y, idx_out, count_out, stream);
 }
 
 pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx, const int32_t* count,

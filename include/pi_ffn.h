@@ -36,7 +36,8 @@
  * - Ownership: the caller allocates ALL device memory (weights, x, y, index
  *   buffers, workspace).  The library never allocates device memory; its only
  *   host allocation is the handle.  A handle borrows the weight and workspace
- *   pointers until pi_ffn_destroy.
+ *   pointers until pi_ffn_destroy.  (pi_ffn_forward_static works instead in a
+ *   file-scope device array of the library, PI_FFN_STATIC_SCRATCH_BYTES per GPU.)
  * - Streams: calls only enqueue work on `stream` (a hipStream_t passed as
  *   void*, NULL = the null stream) and return without synchronising.  A
  *   handle is not safe for concurrent use from two streams: it shares its
@@ -60,7 +61,10 @@
 extern "C" {
 #endif
 
-#define PI_FFN_ABI_VERSION 4
+#define PI_FFN_ABI_VERSION 5
+
+/* Bytes of the device scratch array pi_ffn_forward_static works in, one per GPU. */
+#define PI_FFN_STATIC_SCRATCH_BYTES (16u << 20)
 
 typedef enum pi_status {
   PI_OK = 0,
@@ -179,6 +183,21 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
  */
 pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx,
                                 const int32_t* count, void* y, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid it): pi_ffn_forward without a handle or a caller workspace.  It
+ * works in a file-scope device array of PI_FFN_STATIC_SCRATCH_BYTES bytes, one per GPU, held
+ * until the process ends, and allocates nothing (no hipMalloc, no host allocation).  desc and
+ * weights are validated as by pi_ffn_create; a descriptor whose pi_ffn_workspace_bytes exceeds
+ * PI_FFN_STATIC_SCRATCH_BYTES returns PI_ERR_WORKSPACE before anything is enqueued.  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's contents; the call clears what
+ * must start at zero itself.  Calls that overlap on one GPU (two streams, or two threads) race
+ * on the array and give wrong results: serialise them.  Otherwise as pi_ffn_forward.
+ */
+pi_status pi_ffn_forward_static(const pi_ffn_desc* desc, const pi_ffn_weights* weights, const void* x,
+                                int32_t batch, int32_t mask_mode, void* y, int32_t* idx_out,
+                                int32_t* count_out, void* stream);
 
 /*
  * Measurement aid, not part of the FFN: reads `bytes` of device memory at buf once with

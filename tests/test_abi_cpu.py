@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(pi.LIB, name), f"{name} is declared in pi_ffn.h but not exported"
     assert set(declared_functions()) == set(pi.EXPORTED)
-    assert pi.LIB.pi_ffn_abi_version() == 4
+    assert pi.LIB.pi_ffn_abi_version() == 5
 
 
 def test_struct_layouts_match_header():
@@ -121,6 +121,29 @@ def test_package_fails_loudly_without_library(tmp_path):
     res = subprocess.run([sys.executable, "-c", "import activation_sparse_decode_relu_amd"], cwd=ROOT, env=env,
                          capture_output=True, text=True)
     assert res.returncode != 0 and "ImportError" in res.stderr
+
+
+def test_static_forward_rejects_before_any_gpu_call():
+    """The allocation-free entry point validates on the host: bad descriptors and weights, and a
+    descriptor whose workspace exceeds the static scratch, return before anything is enqueued."""
+    pi = _pi()
+    lib = pi.LIB
+    d = _desc()
+    assert lib.pi_ffn_forward_static(None, ctypes.byref(_weights()), 0x1000, 1, 0, 0x1000, None, None, None) == 1
+    assert lib.pi_ffn_forward_static(ctypes.byref(d), ctypes.byref(_weights(w_gate=None)), 0x1000, 1, 0, 0x1000,
+                                     None, None, None) == 1
+    big = _desc(d_model=8192, d_ffn=28672, max_batch=16)      # Llama2-70B shape at 16 tokens: ~130 MB
+    assert pi.workspace_bytes(big) > pi.binding.STATIC_SCRATCH_BYTES
+    assert lib.pi_ffn_forward_static(ctypes.byref(big), ctypes.byref(_weights()), 0x1000, 1, 0, 0x1000, None, None,
+                                     None) == 2
+    assert "static scratch" in pi.last_error()
+
+
+def test_static_scratch_fits_the_one_token_workloads():
+    """The static scratch holds the workspace of every batch-1 workload shape."""
+    pi = _pi()
+    for dm, n, w in ((4096, 11008, "f16"), (7168, 28672, "f16"), (8192, 32768, "q4g32"), (8192, 28672, "f16")):
+        assert pi.workspace_bytes(_desc(d_model=dm, d_ffn=n, w_dtype=w)) <= pi.binding.STATIC_SCRATCH_BYTES
 
 
 def test_probe_read_validates_on_the_host():
