@@ -28,12 +28,13 @@ PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "group": PI_PHASE_GROUP, "down": 
           "finish": PI_PHASE_FINISH}
 STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_ERR_HIP", 4: "PI_ERR_UNSUPPORTED"}
 
-ABI_VERSION = 5   # PI_FFN_ABI_VERSION of the header this binding follows
+ABI_VERSION = 7   # PI_FFN_ABI_VERSION of the header this binding follows
 STATIC_SCRATCH_BYTES = 16 << 20   # PI_FFN_STATIC_SCRATCH_BYTES
 
 EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",
             "pi_ffn_destroy", "pi_ffn_predict", "pi_ffn_forward", "pi_ffn_forward_masked",
-            "pi_ffn_forward_static", "pi_probe_read", "pi_ffn_launch_plan", "pi_ffn_profile_next")
+            "pi_ffn_forward_static", "pi_probe_read", "pi_ffn_set_hot", "pi_ffn_launch_plan",
+            "pi_ffn_profile_next")
 
 
 class PiDesc(ctypes.Structure):
@@ -81,6 +82,8 @@ def _load() -> ctypes.CDLL:
                                           vp]
     lib.pi_probe_read.restype = st
     lib.pi_probe_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
+    lib.pi_ffn_set_hot.restype = st
+    lib.pi_ffn_set_hot.argtypes = [vp, vp]
     lib.pi_ffn_launch_plan.restype = st
     lib.pi_ffn_launch_plan.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_uint32)]
     lib.pi_ffn_profile_next.restype = st
@@ -185,6 +188,12 @@ class FFNLayer:
     def forward_masked(self, x, idx, count, y, stream=None) -> None:
         check(LIB.pi_ffn_forward_masked(self.handle, _ptr(x), int(x.shape[0]), _ptr(idx), _ptr(count),
                                         _ptr(y), _stream(stream)))
+
+    def set_hot(self, hot_words=None) -> None:
+        """pi_ffn_set_hot: hot_words (int32 device tensor, ceil(n / 32) words, bit i = neuron i) are
+        computed on every predicted-mode call; None clears the set.  The layer keeps a reference."""
+        check(LIB.pi_ffn_set_hot(self.handle, _ptr(hot_words)))
+        self.hot_words = hot_words
 
     def launch_plan(self, batch: int, mode="predicted"):
         """The phases a forward call with this batch and mode launches, in launch order."""

@@ -158,6 +158,7 @@ struct pi_ffn {
   size_t ws_bytes;
   Layout L;
   float thr;
+  const unsigned* hot_words;   // predicted mode: the always-computed neurons (pi_ffn_set_hot), or NULL
   void* prof_start[PI_PHASE_COUNT];
   void* prof_stop[PI_PHASE_COUNT];
 
@@ -239,6 +240,7 @@ pik::GroupArgs group_args(const pi_ffn* h, const void* x, int B) {
   a.G = h->L.group;
   a.nw = h->L.waves;
   a.gated = d.gated;
+  a.hot_words = h->hot_words;
   return a;
 }
 
@@ -521,6 +523,21 @@ pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const i
   }
   if ((st = group_phase(h, pik::MODE_LIST, plan, a, s, &partials)) != PI_OK) return st;
   if ((st = finish_phase(h, batch, partials, y, true, 0, nullptr, nullptr, s)) != PI_OK) return st;
+  return ok();
+}
+
+pi_status pi_ffn_set_hot(pi_ffn* h, const uint32_t* hot_words) {
+  if (h == nullptr) return fail(PI_ERR_INVALID, "handle is NULL");
+  const pi_ffn_desc& d = h->desc;
+  if (hot_words != nullptr) {
+    if ((reinterpret_cast<uintptr_t>(hot_words) & 3u) != 0) return fail(PI_ERR_INVALID, "hot_words is not 4-byte aligned");
+    if (d.rank == 0) return fail(PI_ERR_INVALID, "a hot set needs a predictor (rank > 0) for the other neurons");
+    if (d.max_batch != 1 || !pik::split_supported(d.w_dtype, d.act_dtype, d.p_dtype, 1, d.d_model, d.rank))
+      return fail(PI_ERR_UNSUPPORTED,
+                  "a hot set runs on the one-token path only: max_batch 1, fp16 activations and predictor, "
+                  "fp16 rows with d a multiple of 512 up to 8192 or int4 rows with d a multiple of 2048 up to 8192");
+  }
+  h->hot_words = hot_words;
   return ok();
 }
 

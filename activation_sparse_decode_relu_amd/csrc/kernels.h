@@ -30,6 +30,7 @@ struct GroupArgs {
   float* partial;          // [groups][B][d]
   float thr;
   int p_dtype, d, n, r, B, G, nw, gated, mask_only;
+  const unsigned* hot_words;  // MODE_PRED, one-token split path, optional: bit i = neuron i always computed
 };
 
 // Chunks per lane of a wave's d-slice with nw waves per workgroup (1, 2 or 4), or 0 if d is too large.

@@ -103,15 +103,14 @@ __global__ inline void k_fill_u32(unsigned* p, int n, unsigned v) {
 // chunk of the row is loaded once and applied to every token of the batch
 // (tokens in blocks of 4, NB = the most tokens).
 // ---------------------------------------------------------------------------
+// One wave computes row `row` of h (every token of the batch).
 template <int PT, int AT, int NB, int U>
-__global__ __launch_bounds__(256) void k_pred_hidden(const void* __restrict__ p1, const void* __restrict__ x,
-                                                     int d, int r, int B, float* __restrict__ h) {
+__device__ __forceinline__ void hidden_row(const void* __restrict__ p1, const void* __restrict__ x, int d, int r,
+                                           int B, float* __restrict__ h, int row) {
   using XT = typename VecT<AT>::T;
   constexpr int EPC = WFmt<PT>::EPC;
   constexpr int TB = NB < 4 ? NB : 4;             // tokens per block
   const int lane = threadIdx.x & (WAVE - 1);
-
-  const int row = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
   if (row < r) {
     const int nch = d / EPC;
     const u32x4* wrow = reinterpret_cast<const u32x4*>(static_cast<const char*>(p1) + row_bytes(PT, (size_t)row * d));
@@ -151,6 +150,12 @@ __global__ __launch_bounds__(256) void k_pred_hidden(const void* __restrict__ p1
       if (lane == 0 && t < B) h[(size_t)t * r + row] = fmaxf(s, 0.f);
     }
   }
+}
+
+template <int PT, int AT, int NB, int U>
+__global__ __launch_bounds__(256) void k_pred_hidden(const void* __restrict__ p1, const void* __restrict__ x,
+                                                     int d, int r, int B, float* __restrict__ h) {
+  hidden_row<PT, AT, NB, U>(p1, x, d, r, B, h, blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE);
 }
 
 // ---------------------------------------------------------------------------

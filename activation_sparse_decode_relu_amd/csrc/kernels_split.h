@@ -2,7 +2,8 @@
 // fp16 predictor), after k_pred_hidden in predicted mode:
 //
 //   k_act   every wave on its own: NPW consecutive neurons (or NPW consecutive entries of a
-//           caller's list).  Mask source -> decisions -> mask bits; then, for each selected
+//           caller's list).  Mask source -> decisions -> mask bits (the profile's hot neurons,
+//           if given, are selected without reading their predictor rows); then, for each selected
 //           neuron in order, its gate and up rows (full rows, 16-byte loads per lane), two wave
 //           sums, and a = ReLU(g) * u written to a[neuron] in fp32.  No barrier, no LDS: the
 //           waves of a compute unit drift apart, so predictor rows and gathered rows stream
@@ -34,6 +35,47 @@ constexpr int kActWaves = 4;          // independent waves per k_act workgroup
 constexpr int kDnSeg = 1024;          // list entries of a chunk staged in LDS at a time
 constexpr int kCoherent = 16;         // buffer cache policy sc1: coherent across compute units
 constexpr int kRsrcFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
+
+// ---------------------------------------------------------------------------------------------
+// The gate and up sums of one neuron over the full row, by one wave: every 16-byte piece of both
+// rows (and, int4, their group scales) is requested before any is used.  x comes from the
+// wave's registers (xq) or, XLDS, from the workgroup's LDS copy.
+// ---------------------------------------------------------------------------------------------
+template <int WT, int CPL, bool XLDS>
+__device__ __forceinline__ void gate_up_sums(const GroupArgs& A, int id, bool need_gate, bool need_up,
+                                             const XChunk<WT, DT_F16> (&xq)[XLDS ? 1 : CPL],
+                                             const u32x4* s_x, float& gs, float& us) {
+  constexpr int EPC = WFmt<WT>::EPC;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const size_t rbytes = row_bytes(WT, A.d);
+  const int spr = A.d / 32;
+  const char* wgb = static_cast<const char*>(A.w_gate);
+  const char* wub = static_cast<const char*>(A.w_up);
+  u32x4 wg[CPL], wu[CPL];
+  f16 rsg[CPL], rsu[CPL];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    const int c = lane + q * WAVE;
+    wg[q] = need_gate ? ld_stream(reinterpret_cast<const u32x4*>(wgb + rbytes * id) + c) : u32x4{0, 0, 0, 0};
+    wu[q] = need_up ? ld_stream(reinterpret_cast<const u32x4*>(wub + rbytes * id) + c) : u32x4{0, 0, 0, 0};
+    if constexpr (WT == DT_Q4) {
+      const size_t so = (size_t)id * spr + c;
+      rsg[q] = need_gate ? A.s_gate[so] : (f16)0.f;
+      rsu[q] = need_up ? A.s_up[so] : (f16)0.f;
+    }
+  }
+  float pg = 0.f, pu = 0.f;
+#pragma unroll
+  for (int q = 0; q < CPL; ++q) {
+    XChunk<WT, DT_F16> xl;
+    if constexpr (XLDS) xl.load(reinterpret_cast<const f16*>(s_x) + (size_t)(lane + q * WAVE) * EPC);
+    const XChunk<WT, DT_F16>& xc = XLDS ? xl : xq[XLDS ? 0 : q];
+    if (need_gate) dot_chunk<WT, DT_F16>(pg, wg[q], xc, WT == DT_Q4 ? (float)rsg[q] : 1.f);
+    if (need_up) dot_chunk<WT, DT_F16>(pu, wu[q], xc, WT == DT_Q4 ? (float)rsu[q] : 1.f);
+  }
+  gs = need_gate ? wave_sum(pg) : 0.f;
+  us = need_up ? wave_sum(pu) : 0.f;
+}
 
 // ---------------------------------------------------------------------------------------------
 // k_act
@@ -77,16 +119,22 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
   };
 
   const size_t rbytes = row_bytes(WT, d);
-  const int spr = d / 32;   // int4 scales per row
   const bool gated = A.gated != 0;
 
   // ---- decisions ------------------------------------------------------------------------------
   unsigned sel = 0u;        // bit j: entry j is computed (wave-uniform)
   float gval[NPW];          // exact mode: entry j's pre-activation, including b
   if (MODE == MODE_PRED) {
+    // the profile's hot neurons (if any) are selected whatever the predictor would say, and their
+    // P2 rows are never read
+    unsigned hot = 0u;
+    if (A.hot_words != nullptr) {
+      static_assert(NPW <= 32 && 32 % NPW == 0, "a wave's hot bits lie in one word");
+      hot = (A.hot_words[base / 32] >> (base % 32)) & (m >= 32 ? 0xFFFFFFFFu : ((1u << m) - 1u));
+    }
     int rows[NPW];
 #pragma unroll
-    for (int j = 0; j < NPW; ++j) rows[j] = (j < m) ? base + j : -1;
+    for (int j = 0; j < NPW; ++j) rows[j] = (j < m && !((hot >> j) & 1u)) ? base + j : -1;
     float zacc[NPW][1];
     rows_dot<DT_F16, DT_F32, 1, NPW, 2>(zacc, static_cast<const char*>(A.p2), row_bytes(DT_F16, A.r), nullptr, A.r,
                                          rows, A.h, 0, 1);
@@ -94,8 +142,9 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
     for (int j = 0; j < NPW; ++j) {
       const float z = wave_sum(zacc[j][0]) + lane_f(my_bp, j);
       if (j < m) {
-        if (A.logits != nullptr && lane == 0) A.logits[base + j] = z;
-        if (z > A.thr) sel |= 1u << j;
+        const bool is_hot = (hot >> j) & 1u;
+        if (A.logits != nullptr && lane == 0) A.logits[base + j] = is_hot ? __builtin_inff() : z;
+        if (is_hot || z > A.thr) sel |= 1u << j;
       }
     }
   } else if (MODE == MODE_EXACT) {
@@ -139,37 +188,13 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
 #pragma unroll
     for (int q = 0; q < (XLDS ? 1 : CPL); ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * EPC);
   }
-  const char* wgb = static_cast<const char*>(A.w_gate);
-  const char* wub = static_cast<const char*>(A.w_up);
   unsigned todo = sel;
   while (todo != 0u) {
     const int j = __ffs((int)todo) - 1;
     todo &= todo - 1u;
     const int id = id_of(j);
-    u32x4 wg[CPL], wu[CPL];
-    f16 rsg[CPL], rsu[CPL];
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const int c = lane + q * WAVE;
-      wg[q] = need_gate ? ld_stream(reinterpret_cast<const u32x4*>(wgb + rbytes * id) + c) : u32x4{0, 0, 0, 0};
-      wu[q] = need_up ? ld_stream(reinterpret_cast<const u32x4*>(wub + rbytes * id) + c) : u32x4{0, 0, 0, 0};
-      if constexpr (WT == DT_Q4) {
-        const size_t so = (size_t)id * spr + c;
-        rsg[q] = need_gate ? A.s_gate[so] : (f16)0.f;
-        rsu[q] = need_up ? A.s_up[so] : (f16)0.f;
-      }
-    }
-    float pg = 0.f, pu = 0.f;
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      XChunk<WT, DT_F16> xl;
-      if constexpr (XLDS) xl.load(reinterpret_cast<const f16*>(s_x) + (size_t)(lane + q * WAVE) * EPC);
-      const XChunk<WT, DT_F16>& xc = XLDS ? xl : xq[XLDS ? 0 : q];
-      if (need_gate) dot_chunk<WT, DT_F16>(pg, wg[q], xc, WT == DT_Q4 ? (float)rsg[q] : 1.f);
-      if (need_up) dot_chunk<WT, DT_F16>(pu, wu[q], xc, WT == DT_Q4 ? (float)rsu[q] : 1.f);
-    }
-    const float gs = need_gate ? wave_sum(pg) : 0.f;
-    const float us = need_up ? wave_sum(pu) : 0.f;
+    float gs, us;
+    gate_up_sums<WT, CPL, XLDS>(A, id, need_gate, need_up, xq, s_x, gs, us);
     float a;
     if (MODE == MODE_EXACT) {
       float g = 0.f;

@@ -12,9 +12,10 @@ constexpr int kNPW = 8;          // neurons per k_act wave: one mask byte (16 pe
 constexpr bool kXLds = true;     // k_act: x staged in LDS (in registers: 1 % slower, more VGPRs)
 constexpr int kDnNT = 512;       // k_down: 8 waves per tile (4 waves: 6-35 % slower)
 constexpr int kDnTiles = 256;    // k_down: about one tile per compute unit
-// k_down chunks: fp16, each tile's own mask words (equal counts of the global list: 4-7 % slower);
-// int4, equal counts (3 % faster than own words)
-template <int WT> constexpr bool dn_local() { return WT == DT_F16; }
+// k_down chunks: equal counts of the global list.  Chunks of each tile's own mask words were 4-7 %
+// faster on randomly ordered layers, but a hot-first layout packs the always-firing head into the
+// first words, and its first chunk then held about 8 times the mean (Llama2-70B: 42 us, not 15).
+template <int WT> constexpr bool dn_local() { return false; }
 
 int epc_of(int wt) { return wt == DT_Q4 ? 32 : (wt == DT_F16 ? 8 : 4); }
 

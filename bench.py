@@ -37,19 +37,19 @@ def row_bytes(dt: str, k: int) -> float:
     return k * esize(dt)
 
 
-def step_bytes(cfg, mode: str, B: int, count: int) -> float:
+def step_bytes(cfg, mode: str, B: int, count: int, n_hot: int = 0) -> float:
     """Algorithmic bytes of one layer-step: what the method must move.
 
-    Predictor weights and bias (predicted mode), the dense pre-activation
-    matrix and bias (exact mode), the selected neurons' rows of every matrix
-    the mode touches (q4 scales included) and their fp32 bias, x, y and the
-    index list.  Split partials and other scratch traffic are excluded.
+    Predictor weights and bias (predicted mode; with a hot head of n_hot neurons, only the
+    tail's P2 rows and b_p), the dense pre-activation matrix and bias (exact mode), the selected
+    neurons' rows of every matrix the mode touches (q4 scales included) and their fp32 bias, x,
+    y and the index list.  Split partials and other scratch traffic are excluded.
     """
     d, n, r = cfg.d_model, cfg.d_ffn, cfg.rank
     ea, rb = esize(cfg.act_dtype), row_bytes(cfg.w_dtype, d)
     io = 2 * B * d * ea + 4 * count
     if mode == "predicted":
-        pred = (r * d + n * r) * esize(cfg.p_dtype) + 4 * n
+        pred = (r * d + (n - n_hot) * r) * esize(cfg.p_dtype) + 4 * (n - n_hot)
         rows = (3 if cfg.gated else 2) * rb
         return pred + count * (rows + 4) + io
     if mode == "exact":
@@ -60,7 +60,7 @@ def step_bytes(cfg, mode: str, B: int, count: int) -> float:
     return count * (rows + 4) + io
 
 
-def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases) -> float:
+def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases, n_hot: int = 0) -> float:
     """Algorithmic bytes one launch of a phase's kernel moves.
 
     pred_hidden: P1, x, h.  group: the mask source (P2 + b_p, or the dense
@@ -71,7 +71,8 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases) -> float
     handed between them are scratch).  The finish kernel writes y and the index
     list; on the one-token split path (a down kernel and no finish kernel) the
     down kernel writes them, reading the mask bits to find the list.
-    `phases` is the library's launch plan for the call.
+    `phases` is the library's launch plan for the call.  With a hot head of n_hot neurons
+    (predicted mode) the group kernel reads only the tail's P2 rows and b_p.
     """
     d, n, r = cfg.d_model, cfg.d_ffn, cfg.rank
     ea, rb = esize(cfg.act_dtype), row_bytes(cfg.w_dtype, d)
@@ -84,7 +85,8 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases) -> float
     if phase == "group":
         xb = B * d * ea + n / 8
         if mode == "predicted":
-            return (n * r * esize(cfg.p_dtype) + 4 * n + B * r * 4 + count * ((1 + down + cfg.gated) * rb + 4)
+            tail = n - n_hot
+            return (tail * r * esize(cfg.p_dtype) + 4 * tail + B * r * 4 + count * ((1 + down + cfg.gated) * rb + 4)
                     + xb)
         if mode == "exact":
             return n * rb + 4 * n + count * ((down + cfg.gated) * rb) + xb
@@ -97,6 +99,26 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases) -> float
     if phase == "finish":
         return out
     raise KeyError(phase)
+
+
+def expected_active(p, B: int) -> float:
+    """Expected size of the batch-union mask: sum over neurons of 1 - (1 - p_i)^B."""
+    import numpy as np
+    return float(np.sum(1.0 - (1.0 - np.asarray(p, dtype=np.float64)) ** B))
+
+
+def budget_rank(cfg, p, B: int, frac: float, step: int = 64) -> int:
+    """Per-layer predictor rank under a byte budget: the largest multiple of `step`, at most the
+    workload's rank and at least `step`, whose predictor bytes (P1, P2 and b_p) stay within `frac`
+    of the layer's expected active-row bytes (its firing probabilities standing in for the offline
+    profile).  The pages quote the predictor at under 3 % of the total computation."""
+    d, n = cfg.d_model, cfg.d_ffn
+    active = expected_active(p, B) * ((3 if cfg.gated else 2) * row_bytes(cfg.w_dtype, d) + 4)
+    best = step
+    for r in range(step, cfg.rank + 1, step):
+        if (r * d + n * r) * esize(cfg.p_dtype) + 4 * n <= frac * active:
+            best = r
+    return best
 
 
 def source_hash() -> str:
@@ -200,7 +222,7 @@ def read_ceiling(mib: int = 2048, reps: int = 10) -> float:
     import activation_sparse_decode_relu_amd as pi
     n = mib << 20
     buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
-    sums = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    sums = torch.zeros(512, dtype=torch.int32, device="cuda")
     for _ in range(2):
         pi.probe_read(buf, sums)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -323,6 +345,13 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's own)")
     ap.add_argument("--rank", type=int, default=0,
                     help="override the predictor rank r (0 = the workload's own); for rank sweeps")
+    ap.add_argument("--hot", type=float, default=0.0, metavar="F",
+                    help="hot set: profile each layer on 64 calibration tokens (exact-ReLU firing counts) and "
+                         "compute the neurons that fired on at least F of them without the predictor "
+                         "(predicted mode, batch 1); 0 = off")
+    ap.add_argument("--rank-policy", default="fixed", metavar="fixed|budget:F",
+                    help="per-layer predictor rank: the workload's own (fixed), or per layer the largest rank "
+                         "whose predictor bytes stay within F of the layer's expected active-row bytes")
     ap.add_argument("--profile-tokens", type=int, default=4, help="tokens of the per-kernel event pass")
     ap.add_argument("--repeats", type=int, default=5, help="further timed regions of --steps steps, for the spread")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -361,9 +390,9 @@ def main() -> int:
     import activation_sparse_decode_relu_amd as pi
     from synth import config_by_name, make_layer, make_tokens
 
+    import dataclasses
     cfg = config_by_name(args.config)
     if args.rank:
-        import dataclasses
         cfg = dataclasses.replace(cfg, rank=args.rank,
                                   workload=cfg.workload.replace(f"r={cfg.rank}", f"r={args.rank}"))
     B, mode = args.batch, args.mode
@@ -382,9 +411,25 @@ def main() -> int:
     host_sample = {}
     sample_layers = sorted({0, L // 2})
     ws = None
+    ranks, lcfgs, hots = [], [], []
     for l in range(L):
-        layer = make_layer(cfg, l, with_predictor=(mode == "predicted"))
+        lcfg = cfg
+        if args.rank_policy.startswith("budget:") and mode == "predicted":
+            from synth import firing_probs
+            lcfg = dataclasses.replace(cfg, rank=budget_rank(cfg, firing_probs(cfg, l), B,
+                                                               float(args.rank_policy.split(":", 1)[1])))
+        ranks.append(lcfg.rank)
+        lcfgs.append(lcfg)
+        layer = make_layer(lcfg, l, with_predictor=(mode == "predicted"))
         h = pi.upload_layer(layer, dev, max_batch=B, workspace=ws)
+        n_hot = 0
+        if args.hot > 0 and mode == "predicted":
+            from activation_sparse_decode_relu_amd.hotset import firing_counts, hot_set, hot_words
+            cal = torch.from_numpy(make_tokens(cfg, l, 64, start=cfg.tokens - 64)).to(dev)   # not timed
+            hot = hot_set(firing_counts(h, cal), 64, args.hot)
+            n_hot = int(hot.sum())
+            h.set_hot(torch.from_numpy(hot_words(hot).view(np.int32)).to(dev))
+        hots.append(n_hot)
         ws = h.workspace
         handles.append(h)
         if l in sample_layers and not args.no_cpu:
@@ -442,7 +487,8 @@ def main() -> int:
         repeats.append(e0.elapsed_time(e1) / args.steps)
 
     cnt = counts.cpu().numpy().astype(np.int64)          # [T][L], deterministic per (token, layer)
-    bytes_per_token = np.array([sum(step_bytes(cfg, mode, B, int(cnt[t, l])) for l in range(L)) for t in range(T)])
+    bytes_per_token = np.array([sum(step_bytes(lcfgs[l], mode, B, int(cnt[t, l]), hots[l]) for l in range(L))
+                                for t in range(T)])
     total_bytes = sum(bytes_per_token[k % T] for k in range(args.steps))
     sec = ms / 1e3
     layers_per_s = L * args.steps / sec
@@ -468,7 +514,7 @@ def main() -> int:
             torch.cuda.synchronize()
             for l in range(L):
                 durs.append(starts[l].elapsed_ms(stops[l]) * 1e-3)
-                nbytes.append(phase_bytes(cfg, mode, phase, B, int(cnt[t, l]), plan))
+                nbytes.append(phase_bytes(lcfgs[l], mode, phase, B, int(cnt[t, l]), plan, hots[l]))
         tot_s = sum(durs)
         phase_stats[phase] = {"avg_us": 1e6 * tot_s / len(durs), "min_us": 1e6 * min(durs),
                               "launches": len(durs),
@@ -511,6 +557,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": cfg.workload, "name": cfg.name, "mode": mode, "batch": B, "layers": L,
                    "d_model": cfg.d_model, "d_ffn": cfg.d_ffn, "rank": cfg.rank, "gated": cfg.gated,
+                   "rank_policy": args.rank_policy, "hot_fraction": args.hot,
+                   "mean_hot_neurons": round(float(np.mean(hots)), 1),
+                   "layer_ranks": {str(r): ranks.count(r) for r in sorted(set(ranks))},
                    "act_dtype": cfg.act_dtype, "accumulate": "f32", "distinct_tokens": T,
                    "mean_active_neurons": round(mean_count, 1), "timing": "hipGraph per token, hipEvents"},
         "effective_hbm_gbps": round(gbps, 1),

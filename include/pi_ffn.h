@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define PI_FFN_ABI_VERSION 5
+#define PI_FFN_ABI_VERSION 7
 
 /* Bytes of the device scratch array pi_ffn_forward_static works in, one per GPU. */
 #define PI_FFN_STATIC_SCRATCH_BYTES (16u << 20)
@@ -207,6 +207,24 @@ pi_status pi_ffn_forward_static(const pi_ffn_desc* desc, const pi_ffn_weights* w
  * multiple of 16, 1 <= n_sums <= 65536.
  */
 pi_status pi_probe_read(const void* buf, size_t bytes, uint32_t* sums, int32_t n_sums, void* stream);
+
+/*
+ * Hot set: declare the neurons of this handle's layer that are computed on every PREDICTED-mode
+ * call whatever the predictor says; the predictor decides the rest, and the hot neurons' P2 rows
+ * are never read.  The paper explainer's offline profiling (section "オフラインプロファイリング")
+ * counts how often each neuron fires on calibration inputs and sorts the neurons by that count;
+ * the project page ("コア技術原理") and the paper summary ("Key Results") describe the few hot
+ * neurons that fire on almost every input.  The neurons stay where they are: moving the hot ones
+ * to the front would give a few waves all of them.  hot_words is device memory, ceil(n / 32)
+ * uint32 words, bit b of word w = neuron 32 w + b (bits of neurons >= n ignored), borrowed until
+ * the next call of this function or pi_ffn_destroy; NULL clears the set.  PREDICTED mode then
+ * selects hot neurons joined with {i : z_i > log(tau/(1-tau))}; predict() writes +inf as the hot
+ * neurons' logits.  Other modes are unaffected.  A set needs rank > 0 and the one-token path
+ * (max_batch 1, fp16 activations and predictor, fp16 rows with d a multiple of 512 up to 8192 or
+ * int4 rows with d a multiple of 2048 up to 8192), else PI_ERR_UNSUPPORTED.  Host only; takes
+ * effect from the next call.
+ */
+pi_status pi_ffn_set_hot(pi_ffn* h, const uint32_t* hot_words);
 
 /*
  * Which kernels pi_ffn_forward(h, x, batch, mask_mode, ...) launches, for profiling and

@@ -25,6 +25,7 @@ from .ffn import (
     gamma,
     guard_band_exact,
     guard_band_predictor,
+    hot_mask,
     pre_activations,
     prob_band_exact,
     prob_band_predictor,
@@ -51,6 +52,7 @@ __all__ = [
     "gamma",
     "guard_band_exact",
     "guard_band_predictor",
+    "hot_mask",
     "pre_activations",
     "prob_band_exact",
     "prob_band_predictor",

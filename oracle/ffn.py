@@ -169,11 +169,35 @@ def _layer_weights(layer):
     return w_gate, w_up, w_down_t
 
 
-def forward(layer, x, mode: str = "predicted", weights=None) -> dict:
+def hot_mask(n: int, hot=None) -> np.ndarray:
+    """The always-computed hot neurons as a boolean mask over the n neurons (hot: a boolean mask
+    or a list of neuron ids; None is the empty set).
+
+    The paper explainer's offline profiling (section "オフラインプロファイリング") counts how often
+    each neuron fires on calibration inputs and sorts the neurons by that count; the project page
+    ("コア技術原理") and the paper summary ("Key Results") describe the few hot neurons that fire
+    on almost every input.  The hot set is computed on every token without consulting the
+    predictor.
+    """
+    m = np.zeros(n, dtype=bool)
+    if hot is None:
+        return m
+    hot = np.asarray(hot)
+    if hot.dtype == bool:
+        if hot.shape != (n,):
+            raise ValueError("a hot mask must have one entry per neuron")
+        return hot.copy()
+    m[hot.astype(np.int64)] = True
+    return m
+
+
+def forward(layer, x, mode: str = "predicted", weights=None, hot=None) -> dict:
     """The whole step for a batch x [B][d]: mask -> indices -> activations -> output.
 
     mode: "predicted" (predictor mask), "exact" (mask = ReLU support), "dense" (all
     neurons).  `weights` may pass pre-decoded (w_gate, w_up, w_down_t) float64.
+    hot (predicted mode): neurons selected whatever the predictor says (the profile's hot set,
+    as a boolean mask or id list); the predictor decides the rest.
     Returns idx, count, y64 (float64 [B][d]) and y (rounded to the act dtype),
     plus the intermediate g, u, a and (predicted mode) z.
     """
@@ -185,7 +209,7 @@ def forward(layer, x, mode: str = "predicted", weights=None) -> dict:
     if mode == "predicted":
         z = predictor_logits(xx, layer.p1, layer.p2, layer.b_p)
         out["z"] = z
-        mask = union_mask(predicted_mask(z, layer.tau))
+        mask = union_mask(predicted_mask(z, layer.tau)) | hot_mask(layer.d_ffn, hot)
     elif mode == "exact":
         mask = union_mask(exact_mask(g))
     elif mode == "dense":

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(pi.LIB, name), f"{name} is declared in pi_ffn.h but not exported"
     assert set(declared_functions()) == set(pi.EXPORTED)
-    assert pi.LIB.pi_ffn_abi_version() == 5
+    assert pi.LIB.pi_ffn_abi_version() == 7
 
 
 def test_struct_layouts_match_header():
@@ -112,6 +112,7 @@ def test_null_handle_calls_are_invalid():
     assert pi.LIB.pi_ffn_destroy(None) == 1
     assert pi.LIB.pi_ffn_profile_next(None, 0, None, None) == 1
     assert pi.LIB.pi_ffn_launch_plan(None, 1, 0, None) == 1
+    assert pi.LIB.pi_ffn_set_hot(None, None) == 1
 
 
 def test_package_fails_loudly_without_library(tmp_path):

@@ -108,3 +108,35 @@ def test_bench_refuses_more_than_one_gpu():
     assert res.returncode == 2
     assert "one GPU" in res.stderr or "one MI355X" in res.stderr
     assert res.stdout == ""
+
+
+def test_budget_rank_policy():
+    """The per-layer rank policy: the largest multiple of 64 whose predictor bytes fit the budget,
+    worked by hand for the Llama2-70B shape (expected active 2867 neurons of 3 x 16 KB rows)."""
+    cfg = config_by_name("llama70b")
+    p = firing_probs(cfg, 0)
+    active = bench.expected_active(p, 1) * (3 * 8192 * 2 + 4)
+    per_rank = (8192 + 28672) * 2          # predictor bytes per unit of rank, plus 4 n for b_p
+    for frac in (0.03, 0.2, 0.35, 1.0):
+        r = bench.budget_rank(cfg, p, 1, frac)
+        assert r % 64 == 0 and 64 <= r <= 1024
+        fits = lambda rr: rr * per_rank + 4 * 28672 <= frac * active
+        assert r == 64 or fits(r)
+        assert r == 1024 or not fits(r + 64)
+    assert bench.budget_rank(cfg, p, 1, 0.03) == 64        # the pages' "under 3 %" leaves the smallest rank
+    assert bench.budget_rank(cfg, p, 1, 1.0) == 1024
+
+
+@pytest.mark.parametrize("name", ["llama7b", "falcon40b", "llama70b"])
+def test_phase_bytes_with_a_hot_head(name):
+    """With a hot head the group kernel no longer reads the head's P2 rows and b_p, and the kernels
+    still add up to the step (which no longer reads them either) plus the hand-offs."""
+    cfg = config_by_name(name)
+    count, n_hot = 3000, 704
+    phases = ("pred_hidden", "group", "down")
+    total = sum(bench.phase_bytes(cfg, "predicted", ph, 1, count, phases, n_hot) for ph in phases)
+    step = bench.step_bytes(cfg, "predicted", 1, count, n_hot)
+    handoff = cfg.d_ffn / 8 * 2 + cfg.d_model * 2 + 2 * cfg.rank * 4
+    assert abs(total - (step + handoff)) <= 1, (total, step, handoff)
+    saved = bench.step_bytes(cfg, "predicted", 1, count) - step
+    assert saved == n_hot * (cfg.rank * 2 + 4)

@@ -508,3 +508,51 @@ def test_prob_band_bounds_fp32_predictor():
         for z32 in _f32_orders(h32, p2, b_p, rng):
             assert np.all(np.abs(z32.astype(np.float64) - z64) <= band)
 
+
+
+# ----------------------------------------------------------------------------
+# Hot set (predicted mode with always-computed neurons)
+# ----------------------------------------------------------------------------
+
+def test_hot_set_golden():
+    """The hand-worked layer of tests/golden/tiny_ffn.json, token 0, tau = 0.5: the predictor alone
+    selects {0}; a hot set {1} adds neuron 1, whose g = -1 < 0 contributes 0, so y is unchanged; a
+    hot set {2} adds neuron 2 (a = ReLU(1) * 3 = 3, down row [0, 1, 0, -1]): y = [-3, 3, 0, -9]."""
+    fx = json.load(open(os.path.join(GOLDEN, "tiny_ffn.json")))
+    layer = _layer(gated=True, w_gate=np.array(fx["w_gate"], float), w_up=np.array(fx["w_up"], float),
+                   w_down_t=np.array(fx["w_down_t"], float), b=np.array(fx["b"], float),
+                   p1=np.array(fx["p1"], float), p2=np.array(fx["p2"], float), b_p=np.array(fx["b_p"], float))
+    x = np.array(fx["x"], float)[[0]]
+    for hot, idx, y in ((None, [0], [-3, 0, 0, -6]), ([0], [0], [-3, 0, 0, -6]), ([1], [0, 1], [-3, 0, 0, -6]),
+                        ([2], [0, 2], [-3, 3, 0, -9]), ([0, 1, 2], [0, 1, 2], [-3, 3, 0, -9])):
+        out = oracle.forward(layer, x, "predicted", hot=hot)
+        assert out["idx"].tolist() == idx and out["y64"].tolist() == [y], hot
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_hot_set_limits_and_brute_force(gated):
+    """An empty hot set is the predicted mode; every neuron hot is the dense mode; in between the
+    list is the hot set joined with the predictor's choice, checked in Fraction arithmetic on a
+    dyadic layer (as an id list and as a boolean mask)."""
+    rng = np.random.default_rng(400 + int(gated))
+    d, n, r, B = 6, 9, 4, 2
+    wg = _dyadic(rng, (n, d)) if gated else None
+    wu, wd, b, x = _dyadic(rng, (n, d)), _dyadic(rng, (n, d)), _dyadic(rng, n), _dyadic(rng, (B, d))
+    p1, p2, bp = _dyadic(rng, (r, d)), _dyadic(rng, (n, r)), _dyadic(rng, n)
+    layer = _layer(gated=gated, w_gate=wg, w_up=wu, w_down_t=wd, b=b, p1=p1, p2=p2, b_p=bp)
+    pred = oracle.forward(layer, x, "predicted")
+    assert np.array_equal(oracle.forward(layer, x, "predicted", hot=[])["y64"], pred["y64"])
+    dense = oracle.forward(layer, x, "dense")
+    full = oracle.forward(layer, x, "predicted", hot=np.ones(n, dtype=bool))
+    assert full["idx"].tolist() == list(range(n)) and np.array_equal(full["y64"], dense["y64"])
+    F = Fraction
+    fr = (lambda m: [[F(v) for v in row] for row in m.tolist()])
+    for hot in ([3], [0, 5, 8], [1, 2, 4, 6, 7]):
+        out = oracle.forward(layer, x, "predicted", hot=hot)
+        as_mask = np.zeros(n, dtype=bool)
+        as_mask[hot] = True
+        assert np.array_equal(oracle.forward(layer, x, "predicted", hot=as_mask)["idx"], out["idx"])
+        expect = sorted(set(hot) | set(pred["idx"].tolist()))
+        assert out["idx"].tolist() == expect
+        ref = _brute_masked(x.tolist(), None if wg is None else fr(wg), fr(wu), fr(wd), b.tolist(), gated, expect)
+        assert [[F(v) for v in row] for row in out["y64"]] == ref

@@ -143,3 +143,18 @@ def test_lattice_layer_is_exact(w_dtype):
     # every value is a multiple of 1/8 below 2^21: exact in fp32 under any summation order
     y8 = out["y64"] * 8
     assert np.all(y8 == np.rint(y8)) and np.all(np.abs(y8) < 2 ** 24)
+
+
+def test_hot_set_and_words():
+    """The host side of the hot set: the neurons that fired on at least the given share of the
+    calibration tokens, packed as the library's bit set (bit b of word w = neuron 32 w + b)."""
+    from activation_sparse_decode_relu_amd.hotset import hot_set, hot_words
+    counts = np.array([3, 10, 10, 0, 9, 10, 1, 10, 10, 10, 10, 10, 10, 2] + [0] * 20 + [10])
+    mask = hot_set(counts, 10, 0.99)
+    assert np.flatnonzero(mask).tolist() == [1, 2, 5, 7, 8, 9, 10, 11, 12, 34]
+    assert np.flatnonzero(hot_set(counts, 10, 0.9)).tolist() == [1, 2, 4, 5, 7, 8, 9, 10, 11, 12, 34]
+    words = hot_words(mask)
+    assert words.dtype == np.uint32 and words.size == 2
+    assert words[0] == (1 << 1) | (1 << 2) | (1 << 5) | (1 << 7) | (0b111111 << 7) and words[1] == 1 << 2
+    back = [32 * w + b for w in range(2) for b in range(32) if (int(words[w]) >> b) & 1]
+    assert back == np.flatnonzero(mask).tolist()
