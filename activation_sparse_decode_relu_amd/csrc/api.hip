@@ -255,7 +255,7 @@ Plan plan_for(const pi_ffn* h, int mode, int B) {
   const pi_ffn_desc& d = h->desc;
   Plan p{};
   p.batched = pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank);
-  p.split = !p.batched && pik::split_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank);
+  p.split = !p.batched && pik::split_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank, d.d_ffn);
   return p;
 }
 
@@ -532,7 +532,7 @@ pi_status pi_ffn_set_hot(pi_ffn* h, const uint32_t* hot_words) {
   if (hot_words != nullptr) {
     if ((reinterpret_cast<uintptr_t>(hot_words) & 3u) != 0) return fail(PI_ERR_INVALID, "hot_words is not 4-byte aligned");
     if (d.rank == 0) return fail(PI_ERR_INVALID, "a hot set needs a predictor (rank > 0) for the other neurons");
-    if (d.max_batch != 1 || !pik::split_supported(d.w_dtype, d.act_dtype, d.p_dtype, 1, d.d_model, d.rank))
+    if (d.max_batch != 1 || !pik::split_supported(d.w_dtype, d.act_dtype, d.p_dtype, 1, d.d_model, d.rank, d.d_ffn))
       return fail(PI_ERR_UNSUPPORTED,
                   "a hot set runs on the one-token path only: max_batch 1, fp16 activations and predictor, "
                   "fp16 rows with d a multiple of 512 up to 8192 or int4 rows with d a multiple of 2048 up to 8192");

@@ -74,7 +74,7 @@ struct DownArgs {
 constexpr int kMaxDnChunks = 32;   // list chunks per column slice (partials the last tile adds)
 constexpr int kTicketStride = 64;  // one ticket per 256 bytes: tickets of different slices share no line
 constexpr int kMaxDnSlices = 16;   // column slices of the split path's widest rows (fp16, d = 8192)
-bool split_supported(int wt, int at, int pt, int B, int d, int r);
+bool split_supported(int wt, int at, int pt, int B, int d, int r, int n);
 int split_slices(int wt, int d);
 int split_chunks(int wt, int d);
 hipError_t launch_act(int wt, int mode, const GroupArgs& a, float* abuf, hipStream_t s);

@@ -9,15 +9,15 @@
 //           waves of a compute unit drift apart, so predictor rows and gathered rows stream
 //           together, and many small workgroups let the dispatcher balance the selected
 //           neurons (binomial per wave) across compute units.
-//   k_down  y over (column slice s, chunk c) tiles.  Every tile scans the whole mask (n / 32
-//           words) to find the global ascending list, and takes chunk c of it: list
-//           positions [c * count / C, (c + 1) * count / C), so every chunk holds the same
-//           number of neurons whatever the mask.  For each, the neuron's contiguous piece of
-//           its W_down^T row (one 16-byte load per lane) times a[neuron]; the tile's four
-//           waves are summed in wave order into its partial.  The last tile of a slice to
-//           finish (a ticket counter per slice) sums the C partials in chunk order, rounds y
-//           once to the act dtype and resets the ticket.  Tile (0, 0) also writes the index
-//           list and count.
+//   k_down  y over (column slice s, chunk c) tiles.  With a mask, chunk c is the selected
+//           neurons of mask words [c * W / C, (c + 1) * W / C), which the tile scans itself;
+//           with a list (or dense), list positions [c * count / C, (c + 1) * count / C).  For
+//           each neuron in ascending order, its contiguous piece of its W_down^T row (one
+//           16-byte load per lane, int4 8 bytes) times a[neuron]; the tile's eight waves are
+//           summed in wave order into its partial.  The last tile of a slice to finish (a
+//           ticket counter per slice) sums the C partials in chunk order, rounds y once to the
+//           act dtype and resets the ticket.  Tile (0, 0) also scans the whole mask and writes
+//           the index list and count.
 //
 // Every floating-point sum has one fixed order (a neuron's dot products, the chunk's neurons in
 // list order, the waves, the chunks), so results are the same on every run whichever tile
@@ -34,6 +34,8 @@ namespace pik {
 constexpr int kActWaves = 4;          // independent waves per k_act workgroup
 constexpr int kDnSeg = 1024;          // list entries of a chunk staged in LDS at a time
 constexpr int kCoherent = 16;         // buffer cache policy sc1: coherent across compute units
+constexpr int kStreaming = 2;         // buffer cache policy nt: streamed past the caches
+constexpr int kOutOfRange = (int)0x80000000u;  // offset past any record (rows < 2^31 bytes): reads zero
 constexpr int kRsrcFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data, no swizzle
 
 // ---------------------------------------------------------------------------------------------
@@ -64,6 +66,11 @@ __device__ __forceinline__ void gate_up_sums(const GroupArgs& A, int id, bool ne
       rsu[q] = need_up ? A.s_up[so] : (f16)0.f;
     }
   }
+  // fp16 rows wider than 4096: keep every load above ahead of every use below.  The scheduler
+  // otherwise interleaves them, leaving about a third of the rows in flight per wave (Llama2-70B
+  // shape: 31.7 us for the kernel interleaved, 28.3 us with all loads ahead); for shorter rows
+  // (LLaMA-7B, int4 Falcon-40B) its interleaving is 2-3 % faster.
+  if constexpr (WT == DT_F16 && CPL > 8) __builtin_amdgcn_sched_barrier(0);
   float pg = 0.f, pu = 0.f;
 #pragma unroll
   for (int q = 0; q < CPL; ++q) {
@@ -82,8 +89,11 @@ __device__ __forceinline__ void gate_up_sums(const GroupArgs& A, int id, bool ne
 // ---------------------------------------------------------------------------------------------
 // XLDS: the workgroup stages x in LDS once and the waves read their chunks from there at each
 // selected neuron, instead of each wave holding x in registers (64 VGPRs at d = 8192).
-template <int WT, int CPL, int MODE, int NPW, bool XLDS>
-__global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, float* __restrict__ abuf) {
+// GT: 1 gated, 0 non-gated, -1 read from A.gated.  MINW: waves per SIMD the register use must
+// allow (0: no bound).
+template <int WT, int CPL, int MODE, int NPW, bool XLDS, int GT = -1, int MINW = 0>
+__global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(const GroupArgs A,
+                                                                                 float* __restrict__ abuf) {
   constexpr int EPC = WFmt<WT>::EPC;
   static_assert(NPW == 8 || NPW == 16 || NPW == 32, "mask bits are written as whole bytes");
   const int lane = threadIdx.x & (WAVE - 1);
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(kActWaves * WAVE) void k_act(const GroupArgs A, flo
   };
 
   const size_t rbytes = row_bytes(WT, d);
-  const bool gated = A.gated != 0;
+  const bool gated = GT >= 0 ? GT == 1 : A.gated != 0;
 
   // ---- decisions ------------------------------------------------------------------------------
   unsigned sel = 0u;        // bit j: entry j is computed (wave-uniform)
@@ -220,11 +230,17 @@ template <int WT> struct DnLane;
 template <> struct DnLane<DT_F16> {
   static constexpr int EL = 8;
   typedef u32x4 V;
+  __device__ static V load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreaming));
+  }
   __device__ static void unpack(V w, float (&o)[8]) { Unpack<DT_F16>::run(w, o); }
 };
 template <> struct DnLane<DT_Q4> {
   static constexpr int EL = 16;
   typedef u32x2 V;
+  __device__ static V load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreaming));
+  }
   __device__ static void unpack(V w, float (&o)[16]) {
     const unsigned ws[2] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u};
 #pragma unroll
@@ -323,9 +339,19 @@ __global__ __launch_bounds__(NT) void k_down(const DownArgs D) {
     lo = (int)((long long)chunk * g_total / C);
     hi = (int)((long long)(chunk + 1) * g_total / C);
   }
-  const size_t rbytes = row_bytes(WT, d);
-  const char* wdb = static_cast<const char*>(D.w_down_t) + row_bytes(WT, (size_t)(col_ok ? col : 0));
+  const int rbytes = (int)row_bytes(WT, d);
+  const int cbytes = (int)row_bytes(WT, (size_t)(col_ok ? col : 0));
   const int spr = d / 32;
+  // every load of a batch goes through a buffer resource: an entry past the list (or a column past
+  // d) gets an out-of-range offset and reads zero, so the batch is straight-line code and the
+  // compiler can wait for one batch while the next is in flight (split_supported keeps n rows
+  // under 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(D.w_down_t), 0,
+                                                                        n * rbytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(D.abuf), 0, n * 4,
+                                                                        kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<f16*>(D.s_down), 0, WT == DT_Q4 ? n * spr * 2 : 0, kRsrcFlags);
   float acc[EL];
 #pragma unroll
   for (int e = 0; e < EL; ++e) acc[e] = 0.f;
@@ -372,33 +398,37 @@ __global__ __launch_bounds__(NT) void k_down(const DownArgs D) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u;
-        const int id = i < mine ? s_ids[wave + NWV * i] : -1;
-        const bool ok = id >= 0 && col_ok;
-        bt.w[u] = ok ? ld_stream(reinterpret_cast<const V*>(wdb + rbytes * id)) : V{};
-        bt.a[u] = id >= 0 ? D.abuf[id] : 0.f;
-        if constexpr (WT == DT_Q4) bt.sc[u] = ok ? D.s_down[(size_t)id * spr + col / 32] : (f16)0.f;
+        const int id = s_ids[wave + NWV * min(i, mine - 1)];
+        const bool ok = i < mine && id >= 0;
+        bt.w[u] = LD::load(wrs, ok && col_ok ? id * rbytes + cbytes : kOutOfRange);
+        bt.a[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, ok ? id * 4 : kOutOfRange, 0, 0));
+        if constexpr (WT == DT_Q4)
+          bt.sc[u] = __builtin_bit_cast(f16, __builtin_amdgcn_raw_buffer_load_b16(
+                                                  srs, ok && col_ok ? (id * spr + col / 32) * 2 : kOutOfRange, 0, 0));
       }
     };
     auto apply = [&](int i0, const Batch& bt) {
+      // entries past the list read zero weights and activations: acc + 0 * 0 leaves acc as it is
+      // (acc starts at +0 and a sum that is exactly zero rounds to +0, so acc is never -0)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (i0 + u < mine) {
-          float wf[EL];
-          LD::unpack(bt.w[u], wf);
-          const float as = WT == DT_Q4 ? bt.a[u] * (float)bt.sc[u] : bt.a[u];
+        float wf[EL];
+        LD::unpack(bt.w[u], wf);
+        const float as = WT == DT_Q4 ? bt.a[u] * (float)bt.sc[u] : bt.a[u];
 #pragma unroll
-          for (int e = 0; e < EL; ++e) acc[e] = fmaf(as, wf[e], acc[e]);
-        }
+        for (int e = 0; e < EL; ++e) acc[e] = fmaf(as, wf[e], acc[e]);
       }
     };
-    Batch ba, bb;
-    load(0, ba);
-    for (int i0 = 0; i0 < mine; i0 += 2 * U) {
-      load(i0 + U, bb);
-      apply(i0, ba);
-      if (i0 + U >= mine) break;
-      load(i0 + 2 * U, ba);
-      apply(i0 + U, bb);
+    if (mine > 0) {
+      Batch ba, bb;
+      load(0, ba);
+      for (int i0 = 0; i0 < mine; i0 += 2 * U) {
+        load(i0 + U, bb);
+        apply(i0, ba);
+        if (i0 + U >= mine) break;
+        load(i0 + 2 * U, ba);
+        apply(i0 + U, bb);
+      }
     }
   }
 

@@ -12,10 +12,15 @@ constexpr int kNPW = 8;          // neurons per k_act wave: one mask byte (16 pe
 constexpr bool kXLds = true;     // k_act: x staged in LDS (in registers: 1 % slower, more VGPRs)
 constexpr int kDnNT = 512;       // k_down: 8 waves per tile (4 waves: 6-35 % slower)
 constexpr int kDnTiles = 256;    // k_down: about one tile per compute unit
-// k_down chunks: equal counts of the global list.  Chunks of each tile's own mask words were 4-7 %
-// faster on randomly ordered layers, but a hot-first layout packs the always-firing head into the
-// first words, and its first chunk then held about 8 times the mean (Llama2-70B: 42 us, not 15).
-template <int WT> constexpr bool dn_local() { return false; }
+// k_down chunks: each tile's own range of mask words, so no tile but (0, 0) scans the whole mask.
+// Against equal counts of the global list this was 6 % faster on Llama2-70B (13.0 against
+// 13.8 us), 3 % on Falcon-40B int4 and 1 % on LLaMA-7B, with the neurons' order random under the
+// firing law.  A layout that packed the always-firing neurons into the first words would load
+// the first chunks several times the mean (hot-first Llama2-70B: 42 us, not 15).
+template <int WT> constexpr bool dn_local() { return true; }
+// k_down rows per load batch (two batches in flight): 4 for both formats (fp16: 13.8 against
+// 14.0 us with 8 on Llama2-70B, 7.9 against 8.2 on LLaMA-7B; int4: 12.0 against 14.5)
+constexpr int kDnU = 4;
 
 int epc_of(int wt) { return wt == DT_Q4 ? 32 : (wt == DT_F16 ? 8 : 4); }
 
@@ -32,8 +37,10 @@ int split_slices(int wt, int d) {
   return (d + sw - 1) / sw;
 }
 
-bool split_supported(int wt, int at, int pt, int B, int d, int r) {
+bool split_supported(int wt, int at, int pt, int B, int d, int r, int n) {
   if (B != 1 || at != DT_F16 || (r > 0 && pt != DT_F16)) return false;
+  // k_down addresses a weight matrix (and a, and int4 scales) through 32-bit buffer offsets
+  if ((long long)n * (long long)row_bytes(wt, d) >= (1LL << 31)) return false;
   const int cpl = row_cpl(wt, d);
   bool ok = false;
   if (wt == DT_F16) ok = cpl >= 1 && cpl <= 16;   // d = 512 .. 8192 in steps of 512
@@ -48,13 +55,16 @@ int split_chunks(int wt, int d) {
   return std::max(1, std::min(kMaxDnChunks, (kDnTiles + s - 1) / s));
 }
 
-template <int WT, int MODE>
+// Gated or not is a template argument: with it known, the compiler keeps the Llama2-70B-width
+// kernel at 172 VGPRs instead of 211 and drops a branch around every row load (LLaMA-7B: 11.3
+// against 11.8 us, Falcon-40B int4: 19.8 against 20.7).
+template <int WT, int MODE, int GT>
 static hipError_t act_cpl(const GroupArgs& a, float* abuf, int cpl, hipStream_t s) {
   const int waves = (a.n + kNPW - 1) / kNPW;
   const dim3 grid((waves + kActWaves - 1) / kActWaves), block(kActWaves * WAVE);
   switch (cpl) {
 #define PIK_ACT(C) \
-  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW, kXLds>), grid, block, 0, s, a, abuf); break;
+  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW, kXLds, GT>), grid, block, 0, s, a, abuf); break;
     PIK_ACT(1) PIK_ACT(2) PIK_ACT(3) PIK_ACT(4)
     default:
       if constexpr (WT == DT_F16) {
@@ -71,27 +81,27 @@ static hipError_t act_cpl(const GroupArgs& a, float* abuf, int cpl, hipStream_t 
   return hipGetLastError();
 }
 
-template <int WT>
+template <int WT, int GT>
 static hipError_t act_mode(int mode, const GroupArgs& a, float* abuf, int cpl, hipStream_t s) {
   switch (mode) {
-    case MODE_PRED: return act_cpl<WT, MODE_PRED>(a, abuf, cpl, s);
-    case MODE_EXACT: return act_cpl<WT, MODE_EXACT>(a, abuf, cpl, s);
-    case MODE_DENSE: return act_cpl<WT, MODE_DENSE>(a, abuf, cpl, s);
-    case MODE_LIST: return act_cpl<WT, MODE_LIST>(a, abuf, cpl, s);
+    case MODE_PRED: return act_cpl<WT, MODE_PRED, GT>(a, abuf, cpl, s);
+    case MODE_EXACT: return act_cpl<WT, MODE_EXACT, GT>(a, abuf, cpl, s);
+    case MODE_DENSE: return act_cpl<WT, MODE_DENSE, GT>(a, abuf, cpl, s);
+    case MODE_LIST: return act_cpl<WT, MODE_LIST, GT>(a, abuf, cpl, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_act(int wt, int mode, const GroupArgs& a, float* abuf, hipStream_t s) {
   const int cpl = row_cpl(wt, a.d);
-  if (wt == DT_F16) return act_mode<DT_F16>(mode, a, abuf, cpl, s);
-  if (wt == DT_Q4) return act_mode<DT_Q4>(mode, a, abuf, cpl, s);
+  if (wt == DT_F16) return a.gated ? act_mode<DT_F16, 1>(mode, a, abuf, cpl, s) : act_mode<DT_F16, 0>(mode, a, abuf, cpl, s);
+  if (wt == DT_Q4) return a.gated ? act_mode<DT_Q4, 1>(mode, a, abuf, cpl, s) : act_mode<DT_Q4, 0>(mode, a, abuf, cpl, s);
   return hipErrorInvalidValue;
 }
 
 template <int WT>
 static hipError_t down_mode(int mode, const DownArgs& D, dim3 grid, hipStream_t s) {
-  constexpr int U = WT == DT_Q4 ? 4 : 8;
+  constexpr int U = kDnU;
   const dim3 block(kDnNT);
   switch (mode) {
     case MODE_PRED: hipLaunchKernelGGL((k_down<WT, MODE_PRED, U, kDnNT, dn_local<WT>()>), grid, block, 0, s, D); break;
