@@ -230,16 +230,16 @@ template <int WT> struct DnLane;
 template <> struct DnLane<DT_F16> {
   static constexpr int EL = 8;
   typedef u32x4 V;
-  __device__ static V load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreaming));
+  __device__ static V load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreaming));
   }
   __device__ static void unpack(V w, float (&o)[8]) { Unpack<DT_F16>::run(w, o); }
 };
 template <> struct DnLane<DT_Q4> {
   static constexpr int EL = 16;
   typedef u32x2 V;
-  __device__ static V load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreaming));
+  __device__ static V load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreaming));
   }
   __device__ static void unpack(V w, float (&o)[16]) {
     const unsigned ws[2] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u};
@@ -277,7 +277,9 @@ __global__ __launch_bounds__(NT) void k_down(const DownArgs D) {
   constexpr int SW = dn_slice_cols<WT>();       // columns per slice
   constexpr int NWV = NT / WAVE;                // waves per tile
   constexpr bool kMask = MODE == MODE_PRED || MODE == MODE_EXACT;
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  // the wave index through readfirstlane: known wave-uniform, so a wave's share of the list and
+  // its batch loop live in scalar registers (divided from threadIdx, the loop ran under exec masks)
+  const int lane = threadIdx.x & (WAVE - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int n = D.n, d = D.d, C = D.chunks;
   const int slice = blockIdx.x, chunk = blockIdx.y;
   const int col = slice * SW + lane * EL;       // this lane's first column
@@ -341,11 +343,13 @@ __global__ __launch_bounds__(NT) void k_down(const DownArgs D) {
   }
   const int rbytes = (int)row_bytes(WT, d);
   const int cbytes = (int)row_bytes(WT, (size_t)(col_ok ? col : 0));
+  const int col_oob = col_ok ? 0 : kOutOfRange;
   const int spr = d / 32;
-  // every load of a batch goes through a buffer resource: an entry past the list (or a column past
-  // d) gets an out-of-range offset and reads zero, so the batch is straight-line code and the
-  // compiler can wait for one batch while the next is in flight (split_supported keeps n rows
-  // under 2^31 bytes)
+  // every load of a batch goes through a buffer resource, the row's offset in a scalar register
+  // (an entry is the same for the whole wave) and the lane's column offset in a vector one.  An
+  // entry past the list (or a column past d) gets an out-of-range column offset and reads zero,
+  // so a batch is straight-line code and the compiler can wait for one batch while the next is in
+  // flight (split_supported keeps n rows under 2^31 bytes).
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(D.w_down_t), 0,
                                                                         n * rbytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(D.abuf), 0, n * 4,
@@ -398,13 +402,17 @@ __global__ __launch_bounds__(NT) void k_down(const DownArgs D) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u;
-        const int id = s_ids[wave + NWV * min(i, mine - 1)];
-        const bool ok = i < mine && id >= 0;
-        bt.w[u] = LD::load(wrs, ok && col_ok ? id * rbytes + cbytes : kOutOfRange);
-        bt.a[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, ok ? id * 4 : kOutOfRange, 0, 0));
+        const int id = __builtin_amdgcn_readfirstlane(s_ids[wave + NWV * min(i, mine - 1)]);
+        // the top bit, set when the entry lies past this wave's share or names no neuron, is
+        // or-ed into the column offsets (bit arithmetic, not a select: a select on this
+        // wave-uniform condition becomes a branch around each load)
+        const int oob = ((mine - 1 - i) | id) & kOutOfRange;
+        const int sid = max(id, 0);
+        bt.w[u] = LD::load(wrs, cbytes | oob | col_oob, sid * rbytes);
+        bt.a[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ars, oob, sid * 4, 0));
         if constexpr (WT == DT_Q4)
           bt.sc[u] = __builtin_bit_cast(f16, __builtin_amdgcn_raw_buffer_load_b16(
-                                                  srs, ok && col_ok ? (id * spr + col / 32) * 2 : kOutOfRange, 0, 0));
+                                                  srs, ((col_ok ? col : 0) / 32) * 2 | oob | col_oob, sid * spr * 2, 0));
       }
     };
     auto apply = [&](int i0, const Batch& bt) {
@@ -420,14 +428,20 @@ __global__ __launch_bounds__(NT) void k_down(const DownArgs D) {
       }
     };
     if (mine > 0) {
+      // the scheduling barriers keep each batch's loads where they are written: issued before
+      // the other batch is applied, so the wait before an apply leaves the next batch in flight
       Batch ba, bb;
       load(0, ba);
       for (int i0 = 0; i0 < mine; i0 += 2 * U) {
         load(i0 + U, bb);
+        __builtin_amdgcn_sched_barrier(0);
         apply(i0, ba);
+        __builtin_amdgcn_sched_barrier(0);
         if (i0 + U >= mine) break;
         load(i0 + 2 * U, ba);
+        __builtin_amdgcn_sched_barrier(0);
         apply(i0 + U, bb);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
