@@ -28,7 +28,7 @@ PHASES = {"pred_hidden": PI_PHASE_PRED_HIDDEN, "group": PI_PHASE_GROUP, "down": 
           "finish": PI_PHASE_FINISH}
 STATUS_NAMES = {0: "PI_OK", 1: "PI_ERR_INVALID", 2: "PI_ERR_WORKSPACE", 3: "PI_ERR_HIP", 4: "PI_ERR_UNSUPPORTED"}
 
-ABI_VERSION = 7   # PI_FFN_ABI_VERSION of the header this binding follows
+ABI_VERSION = 8   # PI_FFN_ABI_VERSION of the header this binding follows
 STATIC_SCRATCH_BYTES = 16 << 20   # PI_FFN_STATIC_SCRATCH_BYTES
 
 EXPORTED = ("pi_ffn_abi_version", "pi_last_error", "pi_ffn_workspace_bytes", "pi_ffn_create",

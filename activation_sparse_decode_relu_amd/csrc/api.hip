@@ -49,7 +49,7 @@ pi_status ok() {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxBatch = 16;
+constexpr int kMaxBatch = pik::kMaxBatchTokens;
 constexpr int kMaxD = 1 << 20;
 constexpr int kMaxN = 1 << 24;
 
@@ -94,13 +94,16 @@ Layout layout_for(const pi_ffn_desc& d) {
   L.count = off;   off = align_up(off + sizeof(int));
   // activations handed from the group (or act) kernel to the down kernel: a[neuron][16] fp32 on
   // the batched matrix-core path, a[neuron] on the one-token split path
-  L.abuf = off;    off = align_up(off + sizeof(float) * n * (d.max_batch > 1 ? pik::kMaxTokens : 1));
-  // partials: one [B][d] block per group workgroup, or per down chunk on the batched path;
-  // [chunks][d] on the split path
+  const size_t a_stride = d.max_batch > pik::kMaxTokens ? pik::kMaxBatchTokens : (d.max_batch > 1 ? pik::kMaxTokens : 1);
+  L.abuf = off;    off = align_up(off + sizeof(float) * n * a_stride);
+  // partials: one [B][d] block per group workgroup (vector path, at most 16 tokens), or per down
+  // chunk on the batched path; [chunks][d] on the split path
   L.max_partials = L.n_groups;
   if (d.max_batch > 1) L.max_partials = std::max(L.max_partials, pik::batch_down_chunks(d.d_model));
   const size_t split_part = (size_t)pik::split_chunks(d.w_dtype, d.d_model) * dm;
-  L.partial = off; off = align_up(off + sizeof(float) * std::max((size_t)L.max_partials * B * dm, split_part));
+  const size_t vec_part = (size_t)L.n_groups * std::min(B, (size_t)pik::kMaxTokens) * dm;
+  const size_t batch_part = d.max_batch > 1 ? (size_t)pik::batch_down_chunks(d.d_model) * B * dm : 0;
+  L.partial = off; off = align_up(off + sizeof(float) * std::max(std::max(vec_part, batch_part), split_part));
   L.total = off;
   return L;
 }
@@ -124,6 +127,11 @@ pi_status check_desc(const pi_ffn_desc* d) {
     return fail(PI_ERR_INVALID, "act_dtype=%d must be PI_F32 or PI_F16", d->act_dtype);
   if (d->rank > 0 && !(d->tau > 0.0f && d->tau < 1.0f))
     return fail(PI_ERR_INVALID, "tau=%g must lie in (0, 1)", (double)d->tau);
+  if (d->max_batch > pik::kMaxTokens &&
+      !pik::batch_large_supported(d->w_dtype, d->act_dtype, d->max_batch, d->d_model))
+    return fail(PI_ERR_UNSUPPORTED,
+                "max_batch=%d: more than %d tokens run on the matrix cores only (fp16 weights and activations, "
+                "d_model a multiple of 128)", d->max_batch, pik::kMaxTokens);
   int group, waves;
   group_shape(d->d_ffn, &group, &waves);
   if (pik::group_cpl(d->w_dtype, d->d_model, waves) == 0)
@@ -254,7 +262,8 @@ Plan plan_for(const pi_ffn* h, int mode, int B) {
   (void)mode;
   const pi_ffn_desc& d = h->desc;
   Plan p{};
-  p.batched = pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank);
+  p.batched = pik::batch_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank) ||
+              pik::batch_large_supported(d.w_dtype, d.act_dtype, B, d.d_model);
   p.split = !p.batched && pik::split_supported(d.w_dtype, d.act_dtype, d.p_dtype, B, d.d_model, d.rank, d.d_ffn);
   return p;
 }
@@ -352,6 +361,13 @@ pi_status forward_impl(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mod
       break;
     default:
       return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
+  }
+  if (batch > pik::kMaxTokens && mode == pik::MODE_PRED) {
+    // Past 16 tokens the union of the per-token masks covers most of the layer (about 53 % at
+    // 16 tokens under a 10 % firing rate, 88 % at 64), so every gate row is read anyway: the
+    // predictor is not run, and the exact ReLU support is computed from the dense pre-activations.
+    mode = pik::MODE_EXACT;
+    a.thr = 0.0f;
   }
   int partials = 0;
   const Plan plan = plan_for(h, mode, batch);
@@ -453,6 +469,8 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx, 
                          void* stream) {
   pi_status st = check_call(h, x, batch, nullptr, false);
   if (st != PI_OK) return st;
+  if (batch > pik::kMaxTokens)
+    return fail(PI_ERR_UNSUPPORTED, "batch=%d: the predictor runs on at most %d tokens", batch, pik::kMaxTokens);
   if (h->desc.rank == 0) return fail(PI_ERR_INVALID, "predict needs a predictor (rank > 0)");
   if (idx == nullptr || count == nullptr) return fail(PI_ERR_INVALID, "idx and count are required");
   if ((st = check_int_ptr(idx, "idx")) != PI_OK || (st = check_int_ptr(count, "count")) != PI_OK ||
@@ -509,6 +527,8 @@ pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const i
                                 void* y, void* stream) {
   pi_status st = check_call(h, x, batch, y, true);
   if (st != PI_OK) return st;
+  if (batch > pik::kMaxTokens)
+    return fail(PI_ERR_UNSUPPORTED, "batch=%d: a given list runs on at most %d tokens", batch, pik::kMaxTokens);
   if (idx == nullptr || count == nullptr) return fail(PI_ERR_INVALID, "idx and count are required");
   if ((st = check_int_ptr(idx, "idx")) != PI_OK || (st = check_int_ptr(count, "count")) != PI_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -555,6 +575,7 @@ pi_status pi_ffn_launch_plan(const pi_ffn* h, int32_t batch, int32_t mask_mode, 
     case PI_MASK_DENSE: mode = pik::MODE_DENSE; break;
     default: return fail(PI_ERR_INVALID, "mask_mode=%d is not a pi_mask_mode", mask_mode);
   }
+  if (batch > pik::kMaxTokens && mode == pik::MODE_PRED) mode = pik::MODE_EXACT;   // as pi_ffn_forward
   const Plan p = plan_for(h, mode, batch);
   uint32_t bits = 1u << PI_PHASE_GROUP;
   if (!p.split) bits |= 1u << PI_PHASE_FINISH;

@@ -8,7 +8,8 @@ namespace pik {
 
 enum : int { MODE_PRED = 0, MODE_EXACT = 1, MODE_DENSE = 2, MODE_LIST = 3 };
 
-constexpr int kMaxTokens = 16;
+constexpr int kMaxTokens = 16;        // one MFMA token tile: the predictor, vector and union paths
+constexpr int kMaxBatchTokens = 64;   // the matrix-core path in exact and dense modes (four tiles)
 
 // Everything one k_ffn_group launch reads and writes (passed by value).
 struct GroupArgs {
@@ -43,10 +44,14 @@ hipError_t launch_pred_hidden(int pt, int at, const void* p1, const void* x, int
 
 hipError_t launch_ffn_group(int wt, int at, int mode, const GroupArgs& a, hipStream_t s);
 
-// The batched matrix-core path (2..16 tokens, fp16 weights, activations and predictor):
-// k_ffn_bgroup writes the mask words and a[neuron][16] (fp32) into abuf; k_ffn_bdown writes
-// batch_down_chunks(d) partials of y.
+// The batched matrix-core path (2..16 tokens with fp16 weights, activations and predictor, every
+// mode; 17..64 tokens exact and dense): k_ffn_bgroup writes the mask words and
+// a[neuron][16 batch_tiles(B)] (fp32) into abuf; k_ffn_bdown writes batch_down_chunks(d) partials
+// of y.
 bool batch_supported(int wt, int at, int pt, int B, int d, int r);
+// 17 to 64 tokens (exact and dense modes): fp16 weights and activations, d a multiple of 128.
+bool batch_large_supported(int wt, int at, int B, int d);
+int batch_tiles(int B);   // 16-token tiles of a batch: 1, 2 or 4
 int batch_groups(int n);
 int batch_down_chunks(int d);
 hipError_t launch_ffn_bgroup(int mode, const GroupArgs& a, float* abuf, hipStream_t s);

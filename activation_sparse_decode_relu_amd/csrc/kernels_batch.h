@@ -1,10 +1,13 @@
-// Batched decode steps (2 to 16 tokens; fp16 weights, activations and predictor) on the
+// Batched decode steps (2 to 64 tokens; fp16 weights, activations and predictor) on the
 // CDNA4 matrix cores.
 //
 // With a batch, every gathered row serves B tokens, so the row-gather products become
-// skinny GEMMs.  Tokens are padded to 16, the M dimension of the 16x16 MFMA tiles.  Each
-// of these products must, by construction, contract over the dimension that is contiguous
-// in memory:
+// skinny GEMMs.  Tokens are padded to TT tiles of 16, the M dimension of the 16x16 MFMA
+// tiles: TT = 1 up to 16 tokens (every mode), TT = 2 or 4 up to 32 or 64 tokens (the exact
+// and dense modes: past 16 tokens the union of the per-token masks covers most of the layer,
+// so every row is read and the predictor is not run).  A weight fragment, once loaded, is
+// applied to every token tile.  Each of these products must, by construction, contract over
+// the dimension that is contiguous in memory:
 //
 //   k_ffn_bgroup  one workgroup per group of 64 neurons, 4 waves, each wave taking a
 //                 quarter of the contraction:
@@ -15,7 +18,7 @@
 //                   act   gate and up products of the active neurons (fp16 MFMA, exact
 //                         fp16 products, fp32 accumulation), a fixed-order sum of the four
 //                         waves' partial tiles, a = ReLU(g + b) * u (or ReLU(u + b)),
-//                         written to a[neuron][16] in fp32.
+//                         written to a[neuron][16 TT] in fp32.
 //   k_ffn_bdown   y partials over (neuron chunk, 512-column slice): the contraction runs
 //                 over neurons, which are strided in W_down^T, so it uses the fp32 MFMA
 //                 whose lanes each supply a single element: lane l takes neuron (l / 16) of
@@ -60,27 +63,34 @@ __device__ __forceinline__ float half_at(u32x4 w, int e) { return (float)__built
 // row in use, so a row is requested 64 * BS contiguous bytes at a time rather than 64: operand
 // tiles read in longer row runs stream markedly faster.
 constexpr int kBS = 4;   // MFMA k-steps (of 32) per load batch
+// k-steps per load batch with TT token tiles: fewer with four tiles, whose accumulators take
+// 128 registers
+constexpr int bs_for(int TT) { return TT >= 4 ? 2 : kBS; }
 
-template <int NM, int BS>
-__device__ __forceinline__ void tiles_mma_f16(f32x4 (&acc)[NM][kBT], const f16* const (&w)[NM], const int (&row)[kBT],
-                                              int nt, const f16* __restrict__ x, int B, int K, int k_begin,
-                                              int k_end) {
+template <int NM, int BS, int TT>
+__device__ __forceinline__ void tiles_mma_f16(f32x4 (&acc)[NM][kBT][TT], const f16* const (&w)[NM],
+                                              const int (&row)[kBT], int nt, const f16* __restrict__ x, int B, int K,
+                                              int k_begin, int k_end) {
   const int lane = threadIdx.x & (WAVE - 1), li = lane & 15, lk = lane >> 4;
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int t = 0; t < kBT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const f16* xr = x + (size_t)li * K;
-  const bool xok = li < B;
+    for (int t = 0; t < kBT; ++t)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[m][t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = k_begin; k0 < k_end; k0 += 32 * BS) {
     // step st: lane (li, lk) reads 16 bytes of row li at element k0 + 32 * st + 8 * lk, so the
-    // batch covers 256 contiguous bytes of each row; X is read in the same order
-    u32x4 xa[BS], wv[BS][NM][kBT];
+    // batch covers 64 * BS contiguous bytes of each row; X (token 16 tt + li) in the same order
+    u32x4 xa[BS][TT], wv[BS][NM][kBT];
 #pragma unroll
     for (int st = 0; st < BS; ++st) {
       const int kk = k0 + 32 * st + 8 * lk;
       const bool ok = k0 + 32 * st < k_end;
-      xa[st] = (xok && ok) ? *reinterpret_cast<const u32x4*>(xr + kk) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int tok = 16 * tt + li;
+        xa[st][tt] = (tok < B && ok) ? *reinterpret_cast<const u32x4*>(x + (size_t)tok * K + kk) : u32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -100,7 +110,9 @@ __device__ __forceinline__ void tiles_mma_f16(f32x4 (&acc)[NM][kBT], const f16* 
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int t = 0; t < kBT; ++t)
-          if (t < nt) acc[m][t] = mma_f16(xa[st], wv[st][m][t], acc[m][t]);
+          if (t < nt)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) acc[m][t][tt] = mma_f16(xa[st][tt], wv[st][m][t], acc[m][t][tt]);
   }
 }
 
@@ -112,15 +124,36 @@ __device__ __forceinline__ f32x4 wave_tiles_sum(const f32x4 (*red)[2][kBT][WAVE]
   return s;
 }
 
-template <int MODE>
+// The fixed-order sum over the waves of slot m of every token tile's accumulators: tile tt of
+// this thread's 16-neuron tile (its wave) lands in out[tt].  acc holds this wave's partials of
+// the kBT neuron tiles.
+template <int TT>
+__device__ __forceinline__ void waves_sum_tiles(f32x4 (*red)[2][kBT][WAVE], const f32x4 (&acc)[kBT][TT], int m,
+                                                f32x4 (&out)[TT]) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+    for (int q = 0; q < kBT; ++q) red[wave][m][q][lane] = acc[q][tt];
+    __syncthreads();
+    out[tt] = wave_tiles_sum(red, m, wave, lane);
+    __syncthreads();   // the slots are rewritten for the next token tile
+  }
+}
+
+// TT: token tiles of 16 (B <= 16 TT); above one tile, only the exact and dense modes.
+template <int MODE, int TT>
 __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, float* __restrict__ abuf) {
+  static_assert(TT == 1 || MODE == MODE_EXACT || MODE == MODE_DENSE, "more than 16 tokens: exact or dense only");
+  constexpr int TS = 16 * TT;          // a[neuron][TS]: the activation stride
+  constexpr int BS = bs_for(TT);
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, li = lane & 15, lk = lane >> 4;
   const int B = A.B, d = A.d, n = A.n;
   const int g0 = blockIdx.x * kBG;
   const f16* xb = static_cast<const f16*>(A.x);
 
   __shared__ f32x4 s_red[kBNW][2][kBT][WAVE];   // each wave's partial tiles
-  __shared__ float s_pre[(MODE == MODE_EXACT) ? kBG * kMaxTokens : 1];
+  __shared__ float s_pre[(MODE == MODE_EXACT) ? kBG * TS : 1];
   __shared__ unsigned s_tbits[kBT];
   __shared__ int s_list[kBG];
   __shared__ int s_m;
@@ -129,7 +162,7 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
   if (MODE == MODE_PRED || MODE == MODE_EXACT) {
     // this thread's tile (= its wave) and neuron, after the cross-wave sum
     const int t = wave, nrn = g0 + 16 * t + li;
-    f32x4 z;
+    f32x4 z[TT];
     float bias = 0.f;
     if (MODE == MODE_PRED) {
       if (nrn < n) bias = A.b_p[nrn];
@@ -171,32 +204,31 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
 #pragma unroll
       for (int q = 0; q < kBT; ++q) s_red[wave][0][q][lane] = acc[q];
       __syncthreads();
-      z = wave_tiles_sum(s_red, 0, t, lane);
+      z[0] = wave_tiles_sum(s_red, 0, t, lane);
     } else {
       if (nrn < n) bias = A.b[nrn];
       int row[kBT];
 #pragma unroll
       for (int q = 0; q < kBT; ++q) row[q] = (g0 + 16 * q + li < n) ? g0 + 16 * q + li : -1;
       const f16* const w[1] = {static_cast<const f16*>(A.gated ? A.w_gate : A.w_up)};
-      f32x4 acc[1][kBT];
+      f32x4 acc[1][kBT][TT];
       const int kw = d / kBNW;
-      tiles_mma_f16<1, kBS>(acc, w, row, kBT, xb, B, d, wave * kw, (wave + 1) * kw);
-#pragma unroll
-      for (int q = 0; q < kBT; ++q) s_red[wave][0][q][lane] = acc[0][q];
-      __syncthreads();
-      z = wave_tiles_sum(s_red, 0, t, lane);
+      tiles_mma_f16<1, BS, TT>(acc, w, row, kBT, xb, B, d, wave * kw, (wave + 1) * kw);
+      waves_sum_tiles<TT>(s_red, acc[0], 0, z);
     }
     bool dec = false;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int tok = 4 * lk + v;
-      const float val = z[v] + bias;
-      if (MODE == MODE_EXACT) s_pre[(16 * t + li) * kMaxTokens + tok] = val;
-      if (nrn < n && tok < B) {
-        if (MODE == MODE_PRED && A.logits != nullptr) A.logits[(size_t)tok * n + nrn] = val;
-        dec = dec || (val > A.thr);
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = 16 * tt + 4 * lk + v;
+        const float val = z[tt][v] + bias;
+        if (MODE == MODE_EXACT) s_pre[(16 * t + li) * TS + tok] = val;
+        if (nrn < n && tok < B) {
+          if (MODE == MODE_PRED && A.logits != nullptr) A.logits[(size_t)tok * n + nrn] = val;
+          dec = dec || (val > A.thr);
+        }
       }
-    }
     // neuron li of tile t fires if any of its four lanes (token quarters) saw it fire
     const unsigned long long b = __ballot(dec);
     if (lane == 0) s_tbits[t] = (unsigned)((b | (b >> 16) | (b >> 32) | (b >> 48)) & 0xFFFFull);
@@ -244,55 +276,47 @@ __global__ __launch_bounds__(kBNW * WAVE) void k_ffn_bgroup(const GroupArgs A, f
   const int id = slot < m ? ((MODE == MODE_LIST) ? s_list[slot] : g0 + s_list[slot]) : -1;
   float bj = 0.f;
   if (MODE != MODE_EXACT && id >= 0) bj = A.b[id];
-  f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+  f32x4 g[TT], u[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) g[tt] = u[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // tiles past nt hold zeros: their sums are computed and not used
   if (MODE == MODE_EXACT) {
     if (A.gated) {
       const f16* const w[1] = {static_cast<const f16*>(A.w_up)};
-      f32x4 acc[1][kBT];
-      tiles_mma_f16<1, kBS>(acc, w, row, nt, xb, B, d, kb, kb + kw);
-#pragma unroll
-      for (int q = 0; q < kBT; ++q) s_red[wave][1][q][lane] = acc[0][q];
-      __syncthreads();
-      if (t < nt) u = wave_tiles_sum(s_red, 1, t, lane);
+      f32x4 acc[1][kBT][TT];
+      tiles_mma_f16<1, BS, TT>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+      waves_sum_tiles<TT>(s_red, acc[0], 1, u);
     }
   } else if (A.gated) {
     const f16* const w[2] = {static_cast<const f16*>(A.w_gate), static_cast<const f16*>(A.w_up)};
-    f32x4 acc[2][kBT];
-    tiles_mma_f16<2, kBS>(acc, w, row, nt, xb, B, d, kb, kb + kw);
-#pragma unroll
-    for (int q = 0; q < kBT; ++q) {
-      s_red[wave][0][q][lane] = acc[0][q];
-      s_red[wave][1][q][lane] = acc[1][q];
-    }
-    __syncthreads();
-    if (t < nt) {
-      g = wave_tiles_sum(s_red, 0, t, lane);
-      u = wave_tiles_sum(s_red, 1, t, lane);
-    }
+    f32x4 acc[2][kBT][TT];
+    tiles_mma_f16<2, BS, TT>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+    waves_sum_tiles<TT>(s_red, acc[0], 0, g);
+    waves_sum_tiles<TT>(s_red, acc[1], 1, u);
   } else {
     const f16* const w[1] = {static_cast<const f16*>(A.w_up)};
-    f32x4 acc[1][kBT];
-    tiles_mma_f16<1, kBS>(acc, w, row, nt, xb, B, d, kb, kb + kw);
-#pragma unroll
-    for (int q = 0; q < kBT; ++q) s_red[wave][1][q][lane] = acc[0][q];
-    __syncthreads();
-    if (t < nt) u = wave_tiles_sum(s_red, 1, t, lane);
+    f32x4 acc[1][kBT][TT];
+    tiles_mma_f16<1, BS, TT>(acc, w, row, nt, xb, B, d, kb, kb + kw);
+    waves_sum_tiles<TT>(s_red, acc[0], 1, u);
   }
-  if (id >= 0 && slot < m) {
-    f32x4 a;
+  if (id >= 0 && slot < m && t < nt) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int tok = 4 * lk + v;
-      float av;
-      if (MODE == MODE_EXACT) {
-        const float pre = s_pre[s_list[slot] * kMaxTokens + tok];
-        av = A.gated ? fmaxf(pre, 0.f) * u[v] : fmaxf(pre, 0.f);
-      } else {
-        av = A.gated ? fmaxf(g[v] + bj, 0.f) * u[v] : fmaxf(u[v] + bj, 0.f);
+    for (int tt = 0; tt < TT; ++tt) {
+      f32x4 a;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = 16 * tt + 4 * lk + v;
+        float av;
+        if (MODE == MODE_EXACT) {
+          const float pre = s_pre[s_list[slot] * TS + tok];
+          av = A.gated ? fmaxf(pre, 0.f) * u[tt][v] : fmaxf(pre, 0.f);
+        } else {
+          av = A.gated ? fmaxf(g[tt][v] + bj, 0.f) * u[tt][v] : fmaxf(u[tt][v] + bj, 0.f);
+        }
+        a[v] = tok < B ? av : 0.f;
       }
-      a[v] = tok < B ? av : 0.f;
+      *reinterpret_cast<f32x4*>(abuf + (size_t)id * TS + 16 * tt + 4 * lk) = a;
     }
-    *reinterpret_cast<f32x4*>(abuf + (size_t)id * kMaxTokens + 4 * lk) = a;
   }
 }
 
@@ -307,11 +331,13 @@ constexpr int kDRow = kDW * kDCols;        // 512 columns: a 1 KB fp16 row segme
 constexpr int kDPitch = kDRow + 8;         // LDS row pitch in halves (rows start 16 bytes apart in bank order)
 constexpr int kDRowsPerWave = kDStep / kDW;
 
-template <int MODE>
+// TT: token tiles of 16, as in k_ffn_bgroup (a[neuron][16 TT]).
+template <int MODE, int TT>
 __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restrict__ abuf, const f16* __restrict__ wd,
                                                           const unsigned* __restrict__ mask_words,
                                                           const int* __restrict__ list, const int* __restrict__ list_count,
                                                           int n, int d, int B, float* __restrict__ partial) {
+  constexpr int TS = 16 * TT;
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, li = lane & 15, lk = lane >> 4;
   const int C = gridDim.y, c = blockIdx.y;
   const int cw = blockIdx.x * kDRow;               // first column of the workgroup's slice
@@ -320,11 +346,13 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
   __shared__ int s_list[kDSeg];
   __shared__ int s_cnt;
   __shared__ f16 s_w[2][kDStep][kDPitch];
-  __shared__ float s_a[2][kDStep][kMaxTokens];
+  __shared__ float s_a[2][kDStep][TS];
 
-  f32x4 acc[8];
+  f32x4 acc[8][TT];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[e][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int lo, hi;   // the chunk, in words (mask modes, dense) or list entries (list)
   if (MODE == MODE_LIST) {
@@ -337,10 +365,10 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
     hi = (int)((long long)(c + 1) * nw / C);
   }
   // one step in registers: this wave's kDRowsPerWave rows (16 bytes per lane) and, for the first
-  // 128 threads, 4 tokens' activations of one neuron
+  // 128 threads, 4 tokens' activations of one neuron in each token tile
   struct DRegs {
     u32x4 w[kDRowsPerWave];
-    f32x4 a;
+    f32x4 a[TT];
   };
   constexpr int kSegUnits = (MODE == MODE_LIST) ? kDSeg : kDSeg / 32;
   for (int s0 = lo; s0 < hi; s0 += kSegUnits) {
@@ -387,28 +415,39 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
                      ? ld_stream(reinterpret_cast<const u32x4*>(wd + (size_t)id * d + cw) + lane)
                      : u32x4{0, 0, 0, 0};
       }
-      r.a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) r.a[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (threadIdx.x < kDStep * 4) {
         const int j = j0 + (int)threadIdx.x / 4;
         const int id = j < cnt ? s_list[j] : -1;
-        if (id >= 0) r.a = *reinterpret_cast<const f32x4*>(abuf + (size_t)id * kMaxTokens + 4 * (threadIdx.x % 4));
+        if (id >= 0) {
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            r.a[tt] = *reinterpret_cast<const f32x4*>(abuf + (size_t)id * TS + 16 * tt + 4 * (threadIdx.x % 4));
+        }
       }
     };
     auto stage = [&](const DRegs& r, int buf) {
 #pragma unroll
       for (int i = 0; i < kDRowsPerWave; ++i)
         *reinterpret_cast<u32x4*>(&s_w[buf][wave * kDRowsPerWave + i][8 * lane]) = r.w[i];
-      if (threadIdx.x < kDStep * 4)
-        *reinterpret_cast<f32x4*>(&s_a[buf][threadIdx.x / 4][4 * (threadIdx.x % 4)]) = r.a;
+      if (threadIdx.x < kDStep * 4) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          *reinterpret_cast<f32x4*>(&s_a[buf][threadIdx.x / 4][16 * tt + 4 * (threadIdx.x % 4)]) = r.a[tt];
+      }
     };
     auto mma = [&](int buf) {
       if (!cols) return;
 #pragma unroll
       for (int q = 0; q < kDStep / 4; ++q) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(&s_w[buf][4 * q + lk][wave * kDCols + 8 * li]);
-        const float a = s_a[buf][4 * q + lk][li];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = mma_f32(a, half_at(w, e), acc[e]);
+        for (int tt = 0; tt < TT; ++tt) {
+          const float a = s_a[buf][4 * q + lk][16 * tt + li];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e][tt] = mma_f32(a, half_at(w, e), acc[e][tt]);
+        }
       }
     };
     if (cnt == 0) continue;
@@ -427,17 +466,20 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
     }
   }
   if (!cols) return;
-  // tile e holds columns cw + 128 * wave + 8 * (lane % 16) + e for tokens 4 * (lane / 16) + v
+  // tile (e, tt) holds columns cw + 128 * wave + 8 * (lane % 16) + e for tokens
+  // 16 tt + 4 * (lane / 16) + v
   const int c0 = cw + wave * kDCols;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int tok = 4 * lk + v;
-    if (tok < B) {
-      float* dst = partial + ((size_t)c * B + tok) * d + c0 + 8 * li;
-      *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][v], acc[1][v], acc[2][v], acc[3][v]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4][v], acc[5][v], acc[6][v], acc[7][v]};
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 16 * tt + 4 * lk + v;
+      if (tok < B) {
+        float* dst = partial + ((size_t)c * B + tok) * d + c0 + 8 * li;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0][tt][v], acc[1][tt][v], acc[2][tt][v], acc[3][tt][v]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4][tt][v], acc[5][tt][v], acc[6][tt][v], acc[7][tt][v]};
+      }
     }
-  }
 }
 
 }  // namespace pik

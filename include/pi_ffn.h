@@ -30,7 +30,10 @@
  * - q4g32: each row is d/2 bytes, byte j holding element 2j in bits 0-3 and
  *   element 2j+1 in bits 4-7 as 4-bit two's complement; scales are fp16
  *   [n][d/32], one per 32 consecutive elements; value = q * s.
- * - A batch shares one mask: the union of the per-token masks.
+ * - A batch shares one mask: the union of the per-token masks.  Past 16 tokens
+ *   (max_batch up to 64) that union covers most of a layer, so every row is read
+ *   anyway: a PREDICTED call then runs as EXACT_RELU, without the predictor
+ *   (pi_ffn_forward), and predict / forward_masked take at most 16 tokens.
  * - Index lists are int32, strictly ascending, unique; the count is one int32.
  *   Both live in device memory and are never copied to the host.
  * - Ownership: the caller allocates ALL device memory (weights, x, y, index
@@ -61,7 +64,7 @@
 extern "C" {
 #endif
 
-#define PI_FFN_ABI_VERSION 7
+#define PI_FFN_ABI_VERSION 8
 
 /* Bytes of the device scratch array pi_ffn_forward_static works in, one per GPU. */
 #define PI_FFN_STATIC_SCRATCH_BYTES (16u << 20)
@@ -87,7 +90,7 @@ typedef enum pi_phase {
   PI_PHASE_PRED_HIDDEN = 0, /* h = ReLU(x P1^T)                                        */
   PI_PHASE_GROUP = 1,       /* the mask and the gate/up row gather with a = ReLU(g)*u:
                                one token (fp16 activations, fp16 or int4 rows): k_act;
-                               2..16 tokens on the matrix cores: k_ffn_bgroup; otherwise
+                               2..64 tokens on the matrix cores: k_ffn_bgroup; otherwise
                                k_ffn_group, which also forms each group's partial y     */
   PI_PHASE_DOWN = 2,        /* the down projection over (column slice, neuron chunk)
                                tiles from the activations: one token, k_down (which also
@@ -103,7 +106,8 @@ typedef struct pi_ffn_desc {
   int32_t d_ffn;     /* n: > 0                                                  */
   int32_t rank;      /* r: predictor rank, 0 = no predictor, else multiple of 64 */
   int32_t gated;     /* 1 = gated (W_gate present), 0 = non-gated               */
-  int32_t max_batch; /* 1..16: largest B any call will pass                     */
+  int32_t max_batch; /* 1..64: largest B any call will pass; above 16 only with
+                        fp16 weights and activations and d a multiple of 128       */
   int32_t w_dtype;   /* pi_dtype of W_gate, W_up, W_downT                       */
   int32_t p_dtype;   /* PI_F32 or PI_F16: dtype of P1 and P2                     */
   int32_t act_dtype; /* PI_F32 or PI_F16: dtype of x and y                       */
@@ -156,7 +160,8 @@ pi_status pi_ffn_destroy(pi_ffn* h);
  * inference flow (section "GPU-CPUハイブリッドアーキテクチャ") computes next.  For x [B][d]:
  *   h = ReLU(x P1^T), z = h P2^T + b_p, selected_i = OR_t (z[t][i] > log(tau/(1-tau))),
  * and writes idx[0..count) = ascending selected neurons (capacity n), *count.
- * logits_dbg, if not NULL, receives z as f32 [B][n].  Requires rank > 0.
+ * logits_dbg, if not NULL, receives z as f32 [B][n].  Requires rank > 0 and B <= 16
+ * (PI_ERR_UNSUPPORTED above).
  */
 pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx,
                          int32_t* count, float* logits_dbg, void* stream);
@@ -169,7 +174,10 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx,
  * compaction, the gathered activation a = ReLU(g) (.) u over the selected neurons only, and
  * y[t] = sum over selected i of a[t][i] * W_downT[i], rounded once to act dtype.
  * idx_out (capacity n) and count_out, if not NULL, receive the index list.
- * With no neuron selected, y is +0.0.
+ * With no neuron selected, y is +0.0.  Above 16 tokens a PREDICTED call runs as EXACT_RELU:
+ * the union of the per-token masks covers most of the layer by then (the explainer's power-law
+ * firing makes a few neurons fire for almost every token and the rest at random), so the
+ * predictor would save no rows; idx is then the union of the exact ReLU supports.
  */
 pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode,
                          void* y, int32_t* idx_out, int32_t* count_out, void* stream);
@@ -179,7 +187,8 @@ pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_m
  * "GPU-CPUハイブリッドアーキテクチャ", inference flow step 2) on a caller-given list: idx[0..*count)
  * must be strictly ascending neuron ids in [0, n) (the list is read on the device and not
  * validated; an entry outside [0, n) contributes nothing), 0 <= *count <= n.  Computes the same
- * y as pi_ffn_forward for that list.  count == 0 writes +0.0.
+ * y as pi_ffn_forward for that list.  count == 0 writes +0.0.  B <= 16 (PI_ERR_UNSUPPORTED
+ * above).
  */
 pi_status pi_ffn_forward_masked(pi_ffn* h, const void* x, int32_t batch, const int32_t* idx,
                                 const int32_t* count, void* y, void* stream);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(pi.LIB, name), f"{name} is declared in pi_ffn.h but not exported"
     assert set(declared_functions()) == set(pi.EXPORTED)
-    assert pi.LIB.pi_ffn_abi_version() == 7
+    assert pi.LIB.pi_ffn_abi_version() == 8
 
 
 def test_struct_layouts_match_header():
@@ -49,7 +49,7 @@ def _desc(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(d_model=100), dict(d_model=0), dict(d_ffn=0), dict(rank=65),
-                                 dict(rank=-64), dict(max_batch=0), dict(max_batch=17), dict(w_dtype=7),
+                                 dict(rank=-64), dict(max_batch=0), dict(max_batch=65), dict(w_dtype=7),
                                  dict(p_dtype=2), dict(act_dtype=2), dict(tau=0.0), dict(tau=1.0),
                                  dict(gated=1, w_dtype="q4g32", d_model=96)])
 def test_invalid_descriptors(bad):
@@ -64,9 +64,20 @@ def test_workspace_grows_with_batch_and_rank():
     pi = _pi()
     b1 = pi.workspace_bytes(_desc(max_batch=1))
     b16 = pi.workspace_bytes(_desc(max_batch=16))
+    b64 = pi.workspace_bytes(_desc(max_batch=64))
     r0 = pi.workspace_bytes(_desc(rank=0))
-    assert b16 > b1 > r0 > 0
+    assert b64 > b16 > b1 > r0 > 0
     assert b1 % 256 == 0
+
+
+@pytest.mark.parametrize("bad", [dict(w_dtype="q4g32"), dict(act_dtype="f32"), dict(d_model=4096 + 64)])
+def test_more_than_16_tokens_needs_the_matrix_core_shape(bad):
+    """Past 16 tokens only fp16 weights and activations with d a multiple of 128 are supported."""
+    pi = _pi()
+    assert pi.workspace_bytes(_desc(max_batch=64)) > 0
+    with pytest.raises(pi.PiError) as e:
+        pi.workspace_bytes(_desc(max_batch=17, **bad))
+    assert e.value.status == 4
 
 
 def _create(desc, weights, ws_ptr=None, ws_bytes=0):

@@ -53,6 +53,7 @@ def test_expected_active_counts(name, B, count):
 @pytest.mark.parametrize("name,mode,B,path", [
     ("llama7b", "predicted", 1, "split"), ("falcon40b", "predicted", 1, "split"), ("llama7b", "exact", 1, "split"),
     ("llama70b", "dense", 1, "split"), ("llama70b", "predicted", 16, "batched"), ("llama7b", "exact", 4, "batched"),
+    ("llama70b", "exact", 64, "batched"), ("llama70b", "dense", 32, "batched"),
     ("toy", "predicted", 1, "vector"), ("toy", "exact", 1, "vector")])
 def test_phase_bytes_cover_the_step(name, mode, B, path):
     """The per-kernel algorithmic bytes (the roofline's numerator) add up to the step's bytes
