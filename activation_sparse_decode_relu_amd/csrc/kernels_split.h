@@ -1,14 +1,15 @@
 // The one-token step as two balanced kernels (fp16 activations; fp16 or int4 group-32 weights;
 // fp16 predictor), after k_pred_hidden in predicted mode:
 //
-//   k_act   every wave on its own: NPW consecutive neurons (or NPW consecutive entries of a
-//           caller's list).  Mask source -> decisions -> mask bits (the profile's hot neurons,
-//           if given, are selected without reading their predictor rows); then, for each selected
-//           neuron in order, its gate and up rows (full rows, 16-byte loads per lane), two wave
-//           sums, and a = ReLU(g) * u written to a[neuron] in fp32.  No barrier, no LDS: the
-//           waves of a compute unit drift apart, so predictor rows and gathered rows stream
-//           together, and many small workgroups let the dispatcher balance the selected
-//           neurons (binomial per wave) across compute units.
+//   k_act   every wave: NPW consecutive neurons (or NPW consecutive entries of a caller's
+//           list).  Mask source -> decisions -> mask bits (the profile's hot neurons, if given,
+//           are selected without reading their predictor rows); then, for each selected neuron
+//           in order, its gate and up rows (full rows, 16-byte loads per lane), two wave sums,
+//           and a = ReLU(g) * u written to a[neuron] in fp32.  Gated layers: each wave gathers
+//           its own selected neurons, with no barrier, so the waves of a compute unit drift
+//           apart and predictor rows and gathered rows stream together.  Non-gated layers (one
+//           row per neuron): after one barrier the workgroup's selected neurons are dealt
+//           round-robin to its waves, so no wave gathers several while the others idle.
 //   k_down  y over (column slice s, chunk c) tiles.  With a mask, chunk c is the selected
 //           neurons of mask words [c * W / C, (c + 1) * W / C), which the tile scans itself;
 //           with a list (or dense), list positions [c * count / C, (c + 1) * count / C).  For
@@ -90,12 +91,14 @@ __device__ __forceinline__ void gate_up_sums(const GroupArgs& A, int id, bool ne
 // XLDS: the workgroup stages x in LDS once and the waves read their chunks from there at each
 // selected neuron, instead of each wave holding x in registers (64 VGPRs at d = 8192).
 // GT: 1 gated, 0 non-gated, -1 read from A.gated.  MINW: waves per SIMD the register use must
-// allow (0: no bound).
-template <int WT, int CPL, int MODE, int NPW, bool XLDS, int GT = -1, int MINW = 0>
+// allow (0: no bound).  DEAL: the workgroup's selected neurons are dealt to its waves after a
+// barrier, instead of each wave gathering its own.
+template <int WT, int CPL, int MODE, int NPW, bool XLDS, int GT = -1, int MINW = 0, bool DEAL = false>
 __global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(const GroupArgs A,
                                                                                  float* __restrict__ abuf) {
   constexpr int EPC = WFmt<WT>::EPC;
   static_assert(NPW == 8 || NPW == 16 || NPW == 32, "mask bits are written as whole bytes");
+  static_assert(!DEAL || XLDS, "dealt gathers read x from the workgroup's LDS copy");
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = blockIdx.x * kActWaves + (int)(threadIdx.x / WAVE);
   const int n = A.n, d = A.d;
@@ -109,8 +112,9 @@ __global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(c
   }
   int limit = n;   // neurons (or list entries) that exist
   if (MODE == MODE_LIST) limit = min(max(*A.list_count, 0), n);
-  if (base >= limit) return;
-  const int m = min(NPW, limit - base);
+  const bool live = base < limit;   // dealt: a wave past the end still meets the barrier below
+  if (!DEAL && !live) return;
+  const int m = live ? min(NPW, limit - base) : 0;
 
   // lane j < m holds entry j's neuron id, its FFN bias b and (predicted mode) its predictor bias b_p
   int my_id = -1;
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(c
     // the profile's hot neurons (if any) are selected whatever the predictor would say, and their
     // P2 rows are never read
     unsigned hot = 0u;
-    if (A.hot_words != nullptr) {
+    if (A.hot_words != nullptr && live) {
       static_assert(NPW <= 32 && 32 % NPW == 0, "a wave's hot bits lie in one word");
       hot = (A.hot_words[base / 32] >> (base % 32)) & (m >= 32 ? 0xFFFFFFFFu : ((1u << m) - 1u));
     }
@@ -181,19 +185,59 @@ __global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(c
 
   if (MODE == MODE_PRED || MODE == MODE_EXACT) {
     // this wave's NPW mask bits: whole bytes at neuron base (bits of neurons >= n are 0)
-    if (lane == 0) {
+    if (lane == 0 && live) {
       unsigned char* mb = reinterpret_cast<unsigned char*>(A.mask_words) + base / 8;
       if (NPW == 8) *mb = (unsigned char)sel;
       else if (NPW == 16) *reinterpret_cast<unsigned short*>(mb) = (unsigned short)sel;
       else *reinterpret_cast<unsigned*>(mb) = sel;
     }
   }
-  if (A.mask_only || sel == 0u) return;
-
-  // ---- activations of the selected neurons ------------------------------------------------------
   const bool need_gate = gated && MODE != MODE_EXACT;
   const bool need_up = gated || MODE != MODE_EXACT;   // exact, non-gated: a = ReLU(g) from the mask pass
   XChunk<WT, DT_F16> xq[XLDS ? 1 : CPL];
+  if constexpr (DEAL) {
+    // the workgroup's selected entries, dealt round-robin to its waves in entry order
+    static_assert(NPW * kActWaves <= 32, "one selection word per workgroup");
+    __shared__ unsigned s_sel[kActWaves];
+    __shared__ int s_id[kActWaves * NPW];
+    __shared__ float s_v[kActWaves * NPW];   // bias b, or (exact) the pre-activation
+    const int w = threadIdx.x / WAVE;
+    if (lane == 0) s_sel[w] = A.mask_only ? 0u : sel;
+    if (lane < NPW) {
+      s_id[w * NPW + lane] = my_id;
+      s_v[w * NPW + lane] = my_b;
+    }
+    if (MODE == MODE_EXACT && lane == 0) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) s_v[w * NPW + j] = gval[j];
+    }
+    __syncthreads();
+    unsigned all = 0u;
+#pragma unroll
+    for (int v = 0; v < kActWaves; ++v) all |= s_sel[v] << (NPW * v);
+    const int total = __popc(all);
+    for (int k = w; k < total; k += kActWaves) {
+      unsigned rest = all;
+      for (int q = 0; q < k; ++q) rest &= rest - 1u;   // drop the k lowest set entries
+      const int e = __ffs((int)rest) - 1;
+      const int id = s_id[e];
+      float gs, us;
+      gate_up_sums<WT, CPL, XLDS>(A, id, need_gate, need_up, xq, s_x, gs, us);
+      float a;
+      if (MODE == MODE_EXACT) {
+        const float g = s_v[e];
+        a = gated ? fmaxf(g, 0.f) * us : fmaxf(g, 0.f);
+      } else {
+        const float bj = s_v[e];
+        a = gated ? fmaxf(gs + bj, 0.f) * us : fmaxf(us + bj, 0.f);
+      }
+      if (lane == 0) abuf[id] = a;
+    }
+    return;
+  }
+  if (A.mask_only || sel == 0u) return;
+
+  // ---- activations of the selected neurons ------------------------------------------------------
   if (!XLDS && (need_gate || need_up)) {
 #pragma unroll
     for (int q = 0; q < (XLDS ? 1 : CPL); ++q) xq[q].load(xb + (size_t)(lane + q * WAVE) * EPC);

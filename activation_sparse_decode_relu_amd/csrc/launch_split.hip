@@ -57,14 +57,18 @@ int split_chunks(int wt, int d) {
 
 // Gated or not is a template argument: with it known, the compiler keeps the Llama2-70B-width
 // kernel at 172 VGPRs instead of 211 and drops a branch around every row load (LLaMA-7B: 11.3
-// against 11.8 us, Falcon-40B int4: 19.8 against 20.7).
+// against 11.8 us, Falcon-40B int4: 19.8 against 20.7).  Non-gated layers deal the workgroup's
+// selected neurons to its waves (Falcon-40B int4: 18.7 against 20.0 us, OPT-30B: 16.6 against
+// 16.8); gated layers gather per wave (dealt, Llama2-70B took 29.0 against 28.4 us, LLaMA-7B
+// the same).
 template <int WT, int MODE, int GT>
 static hipError_t act_cpl(const GroupArgs& a, float* abuf, int cpl, hipStream_t s) {
+  constexpr bool kDeal = GT == 0;
   const int waves = (a.n + kNPW - 1) / kNPW;
   const dim3 grid((waves + kActWaves - 1) / kActWaves), block(kActWaves * WAVE);
   switch (cpl) {
 #define PIK_ACT(C) \
-  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW, kXLds, GT>), grid, block, 0, s, a, abuf); break;
+  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW, kXLds, GT, 0, kDeal>), grid, block, 0, s, a, abuf); break;
     PIK_ACT(1) PIK_ACT(2) PIK_ACT(3) PIK_ACT(4)
     default:
       if constexpr (WT == DT_F16) {
