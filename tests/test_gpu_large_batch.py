@@ -5,15 +5,16 @@ predictor.
 
 Integer-lattice layers make every sum exact, so lists and y must match the oracle bit for bit,
 and a 64-token call must equal four 16-token calls bit for bit (a token's y does not depend on
-its batch mates in exact mode).  A random Llama2-70B-shaped layer at 64 tokens checks the
-decisions outside the guard band and y within rel-L2 1e-3 of the oracle on the GPU's own list.
+its batch mates in exact mode).  Random full-size layers (LLaMA-7B and Llama2-70B at 64 tokens,
+OPT-30B non-gated at 32) check the decisions outside the guard band and y within rel-L2 1e-3 of
+the oracle on the GPU's own list, in exact and dense modes.
 """
 
 import numpy as np
 import pytest
 
 import oracle
-from synth import config_by_name, make_lattice_layer, make_lattice_tokens, make_layer, make_tokens
+from synth import config_by_name, firing_probs, make_lattice_layer, make_lattice_tokens, make_layer, make_tokens
 
 from gpu_util import announce, check_decisions, check_idx_valid, rel_l2_rows, run_forward, run_masked, run_predict
 
@@ -99,16 +100,18 @@ def test_predicted_runs_as_exact_past_16_tokens():
     h.close()
 
 
-def test_random_llama70b_layer_64_tokens():
-    cfg = config_by_name("llama70b")
-    announce("large batch: random Llama2-70B layer 0 at 64 tokens, exact and dense")
+@pytest.mark.parametrize("name,B", [("llama7b", 64), ("opt30b", 32), ("llama70b", 64)])
+def test_random_full_size_layer_large_batch(name, B):
+    cfg = config_by_name(name)
+    announce(f"large batch: random {name} layer 0 at {B} tokens, exact and dense")
     layer = make_layer(cfg, 0)
     h = _pi().upload_layer(layer, "cuda", max_batch=64)
     try:
-        x = make_tokens(cfg, 0, 64, start=96)
+        x = make_tokens(cfg, 0, B, start=96)
         idx, count, y = run_forward(h, x, "exact")
         check_idx_valid(idx, count, layer.d_ffn)
-        pre = oracle.dense_weights(layer.w_gate, layer.s_gate)
+        pre = oracle.dense_weights(layer.w_gate, layer.s_gate) if layer.gated else oracle.dense_weights(layer.w_up,
+                                                                                                        layer.s_up)
         g = x.astype(np.float64) @ pre.T + layer.b
         band = oracle.GUARD_SAFETY * oracle.prob_band_exact(x, pre, layer.b)
         del pre
@@ -116,8 +119,9 @@ def test_random_llama70b_layer_64_tokens():
         announce(f"  {inside} of {g.size} token decisions inside the band ({100 * inside / g.size:.3f} %)")
         assert inside <= 0.01 * g.size
         check_decisions(idx, layer.d_ffn, g, band, 0.0)
-        # the union covers most of the layer at 64 tokens
-        assert 0.7 * layer.d_ffn < count < layer.d_ffn
+        # the union of B exact supports covers about sum_i 1 - (1 - p_i)^B of the layer
+        u = float(np.mean(1.0 - (1.0 - firing_probs(cfg, 0)) ** B))
+        assert abs(count / layer.d_ffn - u) < 0.05, (count / layer.d_ffn, u)
         ref = oracle.forward_masked(layer, x, idx)["y64"]
         assert rel_l2_rows(y, ref).max() <= 1e-3
         _, dcount, yd = run_forward(h, x, "dense")
