@@ -101,6 +101,12 @@ def phase_bytes(cfg, mode: str, phase: str, B: int, count: int, phases, n_hot: i
     raise KeyError(phase)
 
 
+def mode_run(mode: str, B: int) -> str:
+    """The mask mode the library runs for a call: past 16 tokens a PREDICTED call runs as EXACT_RELU
+    (the predictor is not run; the union of the per-token masks covers most of the layer there)."""
+    return "exact" if (mode == "predicted" and B > 16) else mode
+
+
 def expected_active(p, B: int) -> float:
     """Expected size of the batch-union mask: sum over neurons of 1 - (1 - p_i)^B."""
     import numpy as np
@@ -396,9 +402,7 @@ def main() -> int:
         cfg = dataclasses.replace(cfg, rank=args.rank,
                                   workload=cfg.workload.replace(f"r={cfg.rank}", f"r={args.rank}"))
     B, mode = args.batch, args.mode
-    # past 16 tokens the library runs a PREDICTED call as EXACT_RELU (no predictor): bytes and the
-    # CPU baseline follow what runs
-    run_mode = "exact" if (mode == "predicted" and B > 16) else mode
+    run_mode = mode_run(mode, B)   # bytes and the CPU baseline follow what runs
     if B not in cfg.batches and not (cfg.name == "toy" and B <= 16):
         print(f"note: batch {B} is not one of {cfg.name}'s configured batches {cfg.batches}", file=sys.stderr)
     L = args.layers or cfg.n_layers

@@ -141,3 +141,13 @@ def test_phase_bytes_with_a_hot_head(name):
     assert abs(total - (step + handoff)) <= 1, (total, step, handoff)
     saved = bench.step_bytes(cfg, "predicted", 1, count) - step
     assert saved == n_hot * (cfg.rank * 2 + 4)
+
+
+def test_mode_run_past_16_tokens():
+    """A PREDICTED call of more than 16 tokens runs as EXACT_RELU; other modes and batches run as asked."""
+    assert bench.mode_run("predicted", 1) == "predicted"
+    assert bench.mode_run("predicted", 16) == "predicted"
+    assert bench.mode_run("predicted", 17) == "exact"
+    assert bench.mode_run("predicted", 64) == "exact"
+    assert bench.mode_run("dense", 64) == "dense"
+    assert bench.mode_run("exact", 32) == "exact"
