@@ -32,7 +32,6 @@
 
 namespace pik {
 
-constexpr int kActWaves = 4;          // independent waves per k_act workgroup
 constexpr int kDnSeg = 1024;          // list entries of a chunk staged in LDS at a time
 constexpr int kCoherent = 16;         // buffer cache policy sc1: coherent across compute units
 constexpr int kStreaming = 2;         // buffer cache policy nt: streamed past the caches
@@ -90,24 +89,23 @@ __device__ __forceinline__ void gate_up_sums(const GroupArgs& A, int id, bool ne
 // ---------------------------------------------------------------------------------------------
 // XLDS: the workgroup stages x in LDS once and the waves read their chunks from there at each
 // selected neuron, instead of each wave holding x in registers (64 VGPRs at d = 8192).
-// GT: 1 gated, 0 non-gated, -1 read from A.gated.  MINW: waves per SIMD the register use must
-// allow (0: no bound).  DEAL: the workgroup's selected neurons are dealt to its waves after a
-// barrier, instead of each wave gathering its own.
-template <int WT, int CPL, int MODE, int NPW, bool XLDS, int GT = -1, int MINW = 0, bool DEAL = false>
-__global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(const GroupArgs A,
-                                                                                 float* __restrict__ abuf) {
+// W: waves per workgroup.  GT: 1 gated, 0 non-gated, -1 read from A.gated.  DEAL: the
+// workgroup's selected neurons are dealt to its waves after a barrier, instead of each wave
+// gathering its own.
+template <int WT, int CPL, int MODE, int NPW, bool XLDS, int W, int GT = -1, bool DEAL = false>
+__global__ __launch_bounds__(W * WAVE) void k_act(const GroupArgs A, float* __restrict__ abuf) {
   constexpr int EPC = WFmt<WT>::EPC;
   static_assert(NPW == 8 || NPW == 16 || NPW == 32, "mask bits are written as whole bytes");
   static_assert(!DEAL || XLDS, "dealt gathers read x from the workgroup's LDS copy");
   const int lane = threadIdx.x & (WAVE - 1);
-  const int wid = blockIdx.x * kActWaves + (int)(threadIdx.x / WAVE);
+  const int wid = blockIdx.x * W + (int)(threadIdx.x / WAVE);
   const int n = A.n, d = A.d;
   const int base = wid * NPW;
   const f16* xb = static_cast<const f16*>(A.x);
   constexpr int kXU = XLDS ? CPL * WAVE * EPC / 8 : 1;   // x as 16-byte units
   __shared__ u32x4 s_x[kXU];
   if constexpr (XLDS) {
-    for (int k = threadIdx.x; k < kXU; k += kActWaves * WAVE) s_x[k] = reinterpret_cast<const u32x4*>(xb)[k];
+    for (int k = threadIdx.x; k < kXU; k += W * WAVE) s_x[k] = reinterpret_cast<const u32x4*>(xb)[k];
     __syncthreads();
   }
   int limit = n;   // neurons (or list entries) that exist
@@ -197,10 +195,10 @@ __global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(c
   XChunk<WT, DT_F16> xq[XLDS ? 1 : CPL];
   if constexpr (DEAL) {
     // the workgroup's selected entries, dealt round-robin to its waves in entry order
-    static_assert(NPW * kActWaves <= 32, "one selection word per workgroup");
-    __shared__ unsigned s_sel[kActWaves];
-    __shared__ int s_id[kActWaves * NPW];
-    __shared__ float s_v[kActWaves * NPW];   // bias b, or (exact) the pre-activation
+    static_assert(NPW * W <= 32, "one selection word per workgroup");
+    __shared__ unsigned s_sel[W];
+    __shared__ int s_id[W * NPW];
+    __shared__ float s_v[W * NPW];   // bias b, or (exact) the pre-activation
     const int w = threadIdx.x / WAVE;
     if (lane == 0) s_sel[w] = A.mask_only ? 0u : sel;
     if (lane < NPW) {
@@ -214,9 +212,9 @@ __global__ __launch_bounds__(kActWaves * WAVE, MINW > 0 ? MINW : 1) void k_act(c
     __syncthreads();
     unsigned all = 0u;
 #pragma unroll
-    for (int v = 0; v < kActWaves; ++v) all |= s_sel[v] << (NPW * v);
+    for (int v = 0; v < W; ++v) all |= s_sel[v] << (NPW * v);
     const int total = __popc(all);
-    for (int k = w; k < total; k += kActWaves) {
+    for (int k = w; k < total; k += W) {
       unsigned rest = all;
       for (int q = 0; q < k; ++q) rest &= rest - 1u;   // drop the k lowest set entries
       const int e = __ffs((int)rest) - 1;

@@ -57,18 +57,32 @@ int split_chunks(int wt, int d) {
 
 // Gated or not is a template argument: with it known, the compiler keeps the Llama2-70B-width
 // kernel at 172 VGPRs instead of 211 and drops a branch around every row load (LLaMA-7B: 11.3
-// against 11.8 us, Falcon-40B int4: 19.8 against 20.7).  Non-gated layers deal the workgroup's
-// selected neurons to its waves (Falcon-40B int4: 18.7 against 20.0 us, OPT-30B: 16.6 against
-// 16.8); gated layers gather per wave (dealt, Llama2-70B took 29.0 against 28.4 us, LLaMA-7B
-// the same).
+// against 11.8 us, Falcon-40B int4: 19.8 against 20.7).  Workgroup shape per row format, timed
+// on each workload's shape:
+//   fp16 gated, rows up to 4096 (LLaMA-7B)      8 waves, per-wave gathers (11.0 against 11.5 us
+//                                               with 4)
+//   fp16 gated, wider rows (Llama2-70B)         4 waves, per-wave gathers (8 waves: 29.0 against
+//                                               28.5; dealt gathers: 29.0)
+//   fp16 non-gated (OPT-30B)                    8 waves, per-wave gathers (16.6 against 17.0 with
+//                                               4 waves dealt, 16.8 with 4 per wave)
+//   int4 (Falcon-40B)                           4 waves, the selected neurons dealt to the waves
+//                                               after a barrier (18.7 against 20.0 per wave)
+template <int WT, int CPL, int GT> struct ActShape {
+  static constexpr bool kDeal = WT == DT_Q4 && GT == 0;
+  static constexpr int kWaves = (WT == DT_F16 && (GT == 0 || CPL <= 8)) ? 8 : 4;
+};
+
 template <int WT, int MODE, int GT>
 static hipError_t act_cpl(const GroupArgs& a, float* abuf, int cpl, hipStream_t s) {
-  constexpr bool kDeal = GT == 0;
   const int waves = (a.n + kNPW - 1) / kNPW;
-  const dim3 grid((waves + kActWaves - 1) / kActWaves), block(kActWaves * WAVE);
   switch (cpl) {
-#define PIK_ACT(C) \
-  case C: hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW, kXLds, GT, 0, kDeal>), grid, block, 0, s, a, abuf); break;
+#define PIK_ACT(C)                                                                                                \
+  case C: {                                                                                                        \
+    using S = ActShape<WT, C, GT>;                                                                                \
+    const dim3 grid((waves + S::kWaves - 1) / S::kWaves), block(S::kWaves * WAVE);                                \
+    hipLaunchKernelGGL((k_act<WT, C, MODE, kNPW, kXLds, S::kWaves, GT, S::kDeal>), grid, block, 0, s, a, abuf);  \
+    break;                                                                                                         \
+  }
     PIK_ACT(1) PIK_ACT(2) PIK_ACT(3) PIK_ACT(4)
     default:
       if constexpr (WT == DT_F16) {
