@@ -24,6 +24,12 @@
 //                 whose lanes each supply a single element: lane l takes neuron (l / 16) of
 //                 a 4-neuron step and 8 consecutive columns of that neuron's row, one
 //                 column per output tile.  a stays fp32; the fp16 weights widen exactly.
+//                 Past 16 tokens that fp32 MFMA would bound the kernel (2 B n d flops), so
+//                 there each 32-neuron step runs on the fp16 MFMA instead: every a is split
+//                 into two fp16 parts, hi = fp16(a) and lo = fp16(a - hi), whose exact
+//                 products with the fp16 weights carry about 22 of a's 24 bits.  A step
+//                 holding an |a| of 2^15 or more (which fp16 cannot split) keeps the fp32
+//                 MFMA, so nothing overflows.
 //
 // The pages describe the single-token step (PowerInfer paper explainer, section
 // "ニューロン活性化のべき乗則分布" for the FFN and "活性化予測器" for the predictor); the
@@ -56,6 +62,8 @@ __device__ __forceinline__ f32x4 mma_f16(u32x4 a, u32x4 b, f32x4 c) {
                                                 0);
 }
 __device__ __forceinline__ float half_at(u32x4 w, int e) { return (float)__builtin_bit_cast(f16x8, w)[e]; }
+// a step's activations from this magnitude on stay on the fp32 MFMA (fp16 tops out at 65504)
+constexpr float kSplitLimit = 32768.f;
 
 // Partial tiles over this wave's share [k_begin, k_end) of a contraction of length K:
 // acc[m][t] += X[tok][k] * W_m[row[t]][k] for the nt tiles in use; rows < 0, tokens >= B and
@@ -338,6 +346,10 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
                                                           const int* __restrict__ list, const int* __restrict__ list_count,
                                                           int n, int d, int B, float* __restrict__ partial) {
   constexpr int TS = 16 * TT;
+  // a of the step in LDS: [neuron][TS] for one token tile; past it [token][kAP] (neurons
+  // contiguous, the row padded by 4 so the lanes' 16-byte reads spread over the banks), the
+  // layout the fp16 MFMA's A operand reads
+  constexpr int kAP = kDStep + 4;
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE, li = lane & 15, lk = lane >> 4;
   const int C = gridDim.y, c = blockIdx.y;
   const int cw = blockIdx.x * kDRow;               // first column of the workgroup's slice
@@ -346,7 +358,10 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
   __shared__ int s_list[kDSeg];
   __shared__ int s_cnt;
   __shared__ f16 s_w[2][kDStep][kDPitch];
-  __shared__ float s_a[2][kDStep][TS];
+  __shared__ __attribute__((aligned(16))) float s_a[2][TT > 1 ? TS * kAP : kDStep * TS];
+  auto a_at = [&](int buf, int nrn, int tok) -> float& {
+    return TT > 1 ? s_a[buf][tok * kAP + nrn] : s_a[buf][nrn * TS + tok];
+  };
 
   f32x4 acc[8][TT];
 #pragma unroll
@@ -427,15 +442,28 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
         }
       }
     };
-    auto stage = [&](const DRegs& r, int buf) {
+    // stages one step; returns whether an activation it staged is too large to split (TT > 1)
+    auto stage = [&](const DRegs& r, int buf) -> int {
 #pragma unroll
       for (int i = 0; i < kDRowsPerWave; ++i)
         *reinterpret_cast<u32x4*>(&s_w[buf][wave * kDRowsPerWave + i][8 * lane]) = r.w[i];
+      int big = 0;
       if (threadIdx.x < kDStep * 4) {
+        const int nrn = threadIdx.x / 4, t4 = 4 * (threadIdx.x % 4);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-          *reinterpret_cast<f32x4*>(&s_a[buf][threadIdx.x / 4][16 * tt + 4 * (threadIdx.x % 4)]) = r.a[tt];
+        for (int tt = 0; tt < TT; ++tt) {
+          if constexpr (TT > 1) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              a_at(buf, nrn, 16 * tt + t4 + v) = r.a[tt][v];
+              big |= fabsf(r.a[tt][v]) >= kSplitLimit ? 1 : 0;
+            }
+          } else {
+            *reinterpret_cast<f32x4*>(&s_a[buf][nrn * TS + t4]) = r.a[tt];
+          }
+        }
       }
+      return big;
     };
     auto mma = [&](int buf) {
       if (!cols) return;
@@ -444,24 +472,65 @@ __global__ __launch_bounds__(kDW * WAVE) void k_ffn_bdown(const float* __restric
         const u32x4 w = *reinterpret_cast<const u32x4*>(&s_w[buf][4 * q + lk][wave * kDCols + 8 * li]);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-          const float a = s_a[buf][4 * q + lk][16 * tt + li];
+          const float a = a_at(buf, 4 * q + lk, 16 * tt + li);
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e][tt] = mma_f32(a, half_at(w, e), acc[e][tt]);
+        }
+      }
+    };
+    // The whole 32-neuron step on the fp16 MFMA (D[16][16] += A[16][32] B[32][16]): tile e of
+    // token tile tt takes A = a[token 16 tt + li][neuron 8 lk + k] and B = W[neuron 8 lk + k]
+    // [column 8 li + e], so its outputs land where the fp32 form puts them.
+    auto mma_split = [&](int buf) {
+      if (!cols) return;
+      // this lane's 8 x 8 block of W: neurons 8 lk .. 8 lk + 7, columns 8 li .. 8 li + 7
+      f16x8 wr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        wr[k] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&s_w[buf][8 * lk + k][wave * kDCols + 8 * li]));
+      u32x4 ahi[TT], alo[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const float* ar = &a_at(buf, 8 * lk, 16 * tt + li);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ar), a1 = *reinterpret_cast<const f32x4*>(ar + 4);
+        const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        f16x8 h, l;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          h[k] = (f16)av[k];
+          l[k] = (f16)(av[k] - (float)h[k]);   // a - fp16(a) is exact in fp32
+        }
+        ahi[tt] = __builtin_bit_cast(u32x4, h);
+        alo[tt] = __builtin_bit_cast(u32x4, l);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        f16x8 b;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) b[k] = wr[k][e];
+        const u32x4 bw = __builtin_bit_cast(u32x4, b);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          acc[e][tt] = mma_f16(ahi[tt], bw, acc[e][tt]);
+          acc[e][tt] = mma_f16(alo[tt], bw, acc[e][tt]);
         }
       }
     };
     if (cnt == 0) continue;
     DRegs r;
     load(r, 0);
-    stage(r, 0);
-    __syncthreads();
+    int big = stage(r, 0);
+    if constexpr (TT > 1) big = __syncthreads_or(big);
+    else __syncthreads();
     int buf = 0;
     for (int j0 = 0; j0 < cnt; j0 += kDStep) {
       const bool more = j0 + kDStep < cnt;   // uniform
       if (more) load(r, j0 + kDStep);
-      mma(buf);
-      if (more) stage(r, buf ^ 1);
-      __syncthreads();
+      if (TT > 1 && !big) mma_split(buf);
+      else mma(buf);
+      const int nbig = more ? stage(r, buf ^ 1) : 0;
+      if constexpr (TT > 1) big = __syncthreads_or(nbig);
+      else __syncthreads();
       buf ^= 1;
     }
   }
