@@ -130,3 +130,31 @@ def test_random_full_size_layer_large_batch(name, B):
     finally:
         h.close()
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B", [20, 40])
+def test_large_activation_step_keeps_fp32(B):
+    """An |a| of 2^15 or more cannot be split into two fp16 parts.  The batched down projection's
+    32-neuron step holding it stays on the fp32 MFMA, the other steps split.  y stays bit-exact on
+    a lattice layer whose one neuron has a of about 40000 on every token."""
+    d, n, r = 512, 1000, 128
+    announce(f"large batch: a step with |a| >= 2^15 keeps fp32, B={B}")
+    layer = make_lattice_layer(d, n, r, False, seed=111)
+    big = 37                                  # in the second 32-neuron step of the first chunk
+    layer.b = np.array(layer.b, copy=True)
+    layer.b[big] = 40000.0                    # a = ReLU(u + b) with u a small integer
+    w = np.array(layer.w_down_t, copy=True)
+    w[big] = 0
+    w[big, 3], w[big, 300] = 1, -1            # y columns 3 and 300 carry about +-40000
+    layer.w_down_t = w
+    x = make_lattice_tokens(d, B, seed=112)
+    h = _pi().upload_layer(layer, "cuda", max_batch=64)
+    for mode in ("dense", "exact"):
+        ref = oracle.forward(layer, x, mode)
+        assert np.all(np.abs(ref["a"][:, big]) >= 32768), "the case does not hold a large activation"
+        idx, count, y = run_forward(h, x, mode)
+        check_idx_valid(idx, count, n)
+        assert count == ref["count"] and np.array_equal(idx, ref["idx"])
+        assert _bitwise(y, ref["y"]), f"{mode}: y differs bitwise from the oracle"
+        assert np.all(np.abs(y[:, 3].astype(np.float64)) > 30000)
+    h.close()
