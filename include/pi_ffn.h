@@ -177,7 +177,10 @@ pi_status pi_ffn_predict(pi_ffn* h, const void* x, int32_t batch, int32_t* idx,
  * With no neuron selected, y is +0.0.  Above 16 tokens a PREDICTED call runs as EXACT_RELU:
  * the union of the per-token masks covers most of the layer by then (the explainer's power-law
  * firing makes a few neurons fire for almost every token and the rest at random), so the
- * predictor would save no rows; idx is then the union of the exact ReLU supports.
+ * predictor would save no rows; idx is then the union of the exact ReLU supports.  Above 16
+ * tokens the down projection also takes each a as two fp16 parts, hi = fp16(a) and
+ * lo = fp16(a - hi), with exact products and f32 accumulation (about 22 of a's 24 bits); a
+ * 32-neuron step holding an |a| of 2^15 or more keeps f32.
  */
 pi_status pi_ffn_forward(pi_ffn* h, const void* x, int32_t batch, int32_t mask_mode,
                          void* y, int32_t* idx_out, int32_t* count_out, void* stream);
