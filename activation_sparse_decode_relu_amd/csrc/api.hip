@@ -135,7 +135,7 @@ pi_status check_desc(const pi_ffn_desc* d) {
   int group, waves;
   group_shape(d->d_ffn, &group, &waves);
   if (pik::group_cpl(d->w_dtype, d->d_model, waves) == 0)
-    return fail(PI_ERR_UNSUPPORTED, "d_model=%d is larger than this build's per-wave slice allows", d->d_model);
+    return fail(PI_ERR_UNSUPPORTED, "d_model=%d is larger than the library's per-wave slice allows", d->d_model);
   return PI_OK;
 }
 

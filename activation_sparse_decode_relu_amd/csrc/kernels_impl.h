@@ -1,9 +1,11 @@
-// gfx950 kernels of the activation-sparse ReLU FFN decode step.
+// gfx950 kernels of the activation-sparse ReLU FFN decode step: the predictor's hidden layer
+// (every route), the vector route and the kernels it shares.  The one-token route's k_act and
+// k_down are in kernels_split.h, the matrix-core batches in kernels_batch.h.
 //
 // The step (PowerInfer paper explainer, section "活性化予測器" for the
 // predictor, section "ニューロン活性化のべき乗則分布" for the FFN equation,
 // section "GPU-CPUハイブリッドアーキテクチャ" for "compute only the predicted
-// neurons"), three kernels per call:
+// neurons"), on the vector route three kernels per call:
 //
 //   k_pred_hidden  h = ReLU(x P1^T)                                   HBM-bound GEMV
 //   k_ffn_group    one workgroup per group of G neurons:

@@ -74,7 +74,7 @@ typedef enum pi_status {
   PI_ERR_INVALID = 1,     /* bad argument; nothing enqueued */
   PI_ERR_WORKSPACE = 2,   /* workspace missing or smaller than pi_ffn_workspace_bytes */
   PI_ERR_HIP = 3,         /* HIP runtime error at launch */
-  PI_ERR_UNSUPPORTED = 4  /* valid request this build does not implement */
+  PI_ERR_UNSUPPORTED = 4  /* valid request the library does not implement */
 } pi_status;
 
 typedef enum pi_dtype { PI_F32 = 0, PI_F16 = 1, PI_Q4G32 = 2 } pi_dtype;
