@@ -164,3 +164,22 @@ def test_probe_read_validates_on_the_host():
     assert pi.LIB.pi_probe_read(0x1008, 16, 0x1000, 1, None) == 1      # misaligned
     assert pi.LIB.pi_probe_read(0x1000, 20, 0x1000, 1, None) == 1      # not whole 16-byte units
     assert pi.LIB.pi_probe_read(0x1000, 16, 0x1000, 0, None) == 1
+
+
+def test_header_is_plain_c(tmp_path):
+    """The boundary is a C ABI: pi_ffn.h compiles as C99 (and as C++) with every warning an error,
+    and a C caller can name every declared entry point."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "use.c"
+    src.write_text('#include "pi_ffn.h"\n'
+                   "typedef void (*any_fn)(void);\n"
+                   "any_fn entry_points[] = {\n" + "".join(f"  (any_fn){n},\n" for n in names) + "};\n")
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I",
+                            os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, f"{lang}: {r.stderr}"
