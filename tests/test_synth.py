@@ -1,6 +1,5 @@
 """The seeded generators reproduce the pages' statistics (CPU only)."""
 
-
 import numpy as np
 import pytest
 from scipy.stats import norm
