@@ -403,6 +403,8 @@ def main() -> int:
                                   workload=cfg.workload.replace(f"r={cfg.rank}", f"r={args.rank}"))
     B, mode = args.batch, args.mode
     run_mode = mode_run(mode, B)   # bytes and the CPU baseline follow what runs
+    if args.hot > 0 and (mode != "predicted" or B != 1):
+        ap.error("--hot applies to the predicted mode at batch 1 (a hot set runs on the one-token route)")
     if B not in cfg.batches and not (cfg.name == "toy" and B <= 16):
         print(f"note: batch {B} is not one of {cfg.name}'s configured batches {cfg.batches}", file=sys.stderr)
     L = args.layers or cfg.n_layers
