@@ -4,6 +4,14 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of the library.  PyTorch supplies device memory and streams.  If the
 library is not built, importing this module raises ImportError: there is no
 fallback.
+
+The C ABI sees bare addresses: it checks their alignment, but it cannot tell
+host memory from device memory or see how large a buffer is, and a kernel that
+reads a host address or writes past a buffer faults the GPU.  So before an
+address is passed, the binding checks that each tensor is a contiguous CUDA
+tensor on the layer's device, of the dtype and with at least the bytes the
+call reads or writes; a failed check raises PiError(PI_ERR_INVALID) and
+nothing is enqueued.
 """
 
 from __future__ import annotations
@@ -125,6 +133,45 @@ def _ptr(t) -> Optional[int]:
     return int(t.data_ptr())
 
 
+_ACT_TORCH = {PI_F32: "float32", PI_F16: "float16"}   # act_dtype -> torch dtype of x and y
+_ELEM_BYTES = {PI_F32: 4, PI_F16: 2}
+
+
+def _invalid(msg: str) -> PiError:
+    return PiError(PI_ERR_INVALID, msg)
+
+
+def _arg(t, name: str, device, nbytes: int = 0, dtype: Optional[str] = None) -> None:
+    """Raise PiError(PI_ERR_INVALID) unless `t` (None passes: the library decides whether the
+    argument may be NULL) is a contiguous torch tensor on `device`, of torch dtype `dtype` if
+    given, holding at least `nbytes` bytes."""
+    if t is None:
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise _invalid(f"{name} must be a torch tensor, not {type(t).__name__}")
+    if t.device != device:
+        raise _invalid(f"{name} is on {t.device}, the layer is on {device}")
+    if not t.is_contiguous():
+        raise _invalid(f"{name} is not contiguous")
+    if dtype is not None and t.dtype != getattr(torch, dtype):
+        raise _invalid(f"{name} is {t.dtype}, expected torch.{dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise _invalid(f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
+def _weight_bytes(desc: PiDesc) -> dict:
+    """Bytes each weight tensor holds under the header's layouts (the descriptor is valid: the
+    library has accepted it)."""
+    n, d, r = desc.d_ffn, desc.d_model, desc.rank
+    row = {PI_F32: 4 * d, PI_F16: 2 * d, PI_Q4G32: d // 2}[desc.w_dtype]
+    scales = n * (d // 32) * 2 if desc.w_dtype == PI_Q4G32 else 0
+    pe = _ELEM_BYTES.get(desc.p_dtype, 0)
+    return dict(w_gate=n * row, w_up=n * row, w_down_t=n * row, s_gate=scales, s_up=scales, s_down=scales,
+                b=4 * n, p1=r * d * pe, p2=n * r * pe, b_p=4 * n)
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -145,9 +192,18 @@ class FFNLayer:
         self.desc = desc
         self.tensors = dict(tensors)
         need = workspace_bytes(desc)
+        given = [t for t in self.tensors.values() if t is not None]
+        if not given or not isinstance(given[0], torch.Tensor) or given[0].device.type != "cuda":
+            raise _invalid("the weights must be CUDA tensors")
+        self.device = given[0].device
+        sizes = _weight_bytes(desc)
+        for k, t in self.tensors.items():
+            if k not in sizes:
+                raise _invalid(f"unknown weight tensor {k!r}")
+            _arg(t, k, self.device, sizes[k])
         if workspace is None:
-            dev = next(t.device for t in self.tensors.values() if t is not None)
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        _arg(workspace, "workspace", self.device)
         self.workspace = workspace
         w = PiWeights(*[_ptr(self.tensors.get(k)) for k, _ in PiWeights._fields_])
         self.weights = w
@@ -168,12 +224,33 @@ class FFNLayer:
         except Exception:
             pass
 
+    def _x(self, x) -> int:
+        """Check x [B][d] (act dtype) and return B."""
+        _arg(x, "x", self.device, dtype=_ACT_TORCH.get(self.desc.act_dtype))
+        if x is None or x.dim() != 2 or x.shape[1] != self.desc.d_model:
+            shape = None if x is None else tuple(x.shape)
+            raise _invalid(f"x must be [B][{self.desc.d_model}], got {shape}")
+        return int(x.shape[0])
+
+    def _y(self, y, B: int) -> None:
+        _arg(y, "y", self.device, B * self.desc.d_model * _ELEM_BYTES.get(self.desc.act_dtype, 0),
+             _ACT_TORCH.get(self.desc.act_dtype))
+
+    def _list(self, idx, count, idx_entries: int) -> None:
+        _arg(idx, "idx", self.device, 4 * idx_entries, "int32")
+        _arg(count, "count", self.device, 4, "int32")
+
     def predict(self, x, idx, count, logits_dbg=None, stream=None) -> None:
+        B = self._x(x)
+        self._list(idx, count, self.desc.d_ffn)
+        _arg(logits_dbg, "logits_dbg", self.device, 4 * B * self.desc.d_ffn, "float32")
         check(LIB.pi_ffn_predict(self.handle, _ptr(x), int(x.shape[0]), _ptr(idx), _ptr(count),
                                  _ptr(logits_dbg), _stream(stream)))
 
     def forward(self, x, y, mode="predicted", idx_out=None, count_out=None, stream=None) -> None:
         m = MODES[mode] if isinstance(mode, str) else int(mode)
+        self._y(y, self._x(x))
+        self._list(idx_out, count_out, self.desc.d_ffn)
         check(LIB.pi_ffn_forward(self.handle, _ptr(x), int(x.shape[0]), m, _ptr(y), _ptr(idx_out),
                                  _ptr(count_out), _stream(stream)))
 
@@ -181,17 +258,24 @@ class FFNLayer:
         """pi_ffn_forward_static with this layer's descriptor and weights (the handle's workspace
         is not used: the call works in the library's static scratch array)."""
         m = MODES[mode] if isinstance(mode, str) else int(mode)
+        self._y(y, self._x(x))
+        self._list(idx_out, count_out, self.desc.d_ffn)
         check(LIB.pi_ffn_forward_static(ctypes.byref(self.desc), ctypes.byref(self.weights), _ptr(x),
                                         int(x.shape[0]), m, _ptr(y), _ptr(idx_out), _ptr(count_out),
                                         _stream(stream)))
 
     def forward_masked(self, x, idx, count, y, stream=None) -> None:
+        """idx holds the list on the device; its length *count is not read on the host, so only
+        the first entry's room is checked here."""
+        self._y(y, self._x(x))
+        self._list(idx, count, 1)
         check(LIB.pi_ffn_forward_masked(self.handle, _ptr(x), int(x.shape[0]), _ptr(idx), _ptr(count),
                                         _ptr(y), _stream(stream)))
 
     def set_hot(self, hot_words=None) -> None:
         """pi_ffn_set_hot: hot_words (int32 device tensor, ceil(n / 32) words, bit i = neuron i) are
         computed on every predicted-mode call; None clears the set.  The layer keeps a reference."""
+        _arg(hot_words, "hot_words", self.device, 4 * ((self.desc.d_ffn + 31) // 32), "int32")
         check(LIB.pi_ffn_set_hot(self.handle, _ptr(hot_words)))
         self.hot_words = hot_words
 
@@ -235,5 +319,10 @@ def upload_layer(layer, device="cuda", max_batch=1, workspace=None, stream=None,
 def probe_read(buf, sums, stream=None) -> None:
     """pi_probe_read: read every byte of the device tensor `buf` once; sums (uint32 device tensor)
     receives one word-sum per workgroup."""
+    import torch
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda":
+        raise _invalid("buf must be a CUDA tensor")
+    _arg(buf, "buf", buf.device)
+    _arg(sums, "sums", buf.device, 4, "int32")
     check(LIB.pi_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sums), int(sums.numel()),
                             _stream(stream)))

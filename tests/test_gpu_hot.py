@@ -78,8 +78,12 @@ def test_set_hot_validation():
     hb.close()
     h = pi.upload_layer(layer, "cuda", max_batch=1)
     with pytest.raises(pi.PiError) as e:
-        h.set_hot(torch.zeros(64, dtype=torch.uint8, device="cuda")[1:])   # misaligned words
+        h.set_hot(torch.zeros(64, dtype=torch.uint8, device="cuda")[1:])   # bytes, not words: the binding
     assert e.value.status == 1
+    # the library's own check, past the binding: an address 2 bytes into a large enough word buffer
+    room = torch.zeros(words.numel() + 1, dtype=torch.int32, device="cuda")
+    assert pi.LIB.pi_ffn_set_hot(h.handle, room.data_ptr() + 2) == 1
+    assert "aligned" in pi.last_error()
     h.close()
 
 
