@@ -136,6 +136,13 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def counters_apply(rank: int, rank_policy: str, hot: float) -> bool:
+    """Whether stored counter bytes describe this run: they were taken on each workload as
+    configured, and a changed predictor rank, a per-layer rank policy or a hot set changes how many
+    predictor bytes the kernels read."""
+    return rank == 0 and rank_policy == "fixed" and hot == 0
+
+
 def stored_traffic(kernel_phase: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they match the current kernels."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -535,7 +542,7 @@ def main() -> int:
     sum_kernels_us = sum(v["avg_us"] for v in phase_stats.values())
 
     workload = f"{cfg.name}-{mode}-b{B}"
-    traffic = stored_traffic(dom, workload)
+    traffic = stored_traffic(dom, workload) if counters_apply(args.rank, args.rank_policy, args.hot) else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ds["achieved_gbps"], 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(ds["achieved_gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "avg_launch_us": round(ds["avg_us"], 3),

@@ -151,3 +151,12 @@ def test_mode_run_past_16_tokens():
     assert bench.mode_run("predicted", 64) == "exact"
     assert bench.mode_run("dense", 64) == "dense"
     assert bench.mode_run("exact", 32) == "exact"
+
+
+def test_stored_counters_only_for_the_profiled_configuration():
+    """Counter bytes were taken on each workload as configured; a changed rank, a rank policy or a
+    hot set reads other predictor bytes, so the bench line's traffic is then null."""
+    assert bench.counters_apply(0, "fixed", 0.0)
+    assert not bench.counters_apply(256, "fixed", 0.0)
+    assert not bench.counters_apply(0, "budget:0.03", 0.0)
+    assert not bench.counters_apply(0, "fixed", 0.99)
