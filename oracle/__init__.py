@@ -11,7 +11,7 @@ brute force on tiny layers, special cases that reduce to a textbook routine,
 invariants of the definition, and the floating-point error bound).
 """
 
-from .ffn import (
+from .ffn import (  # noqa: F401
     GUARD_SAFETY,
     activations,
     certain_union,
@@ -37,30 +37,3 @@ from .ffn import (
     threshold_logit,
     union_mask,
 )
-
-__all__ = [
-    "GUARD_SAFETY",
-    "activations",
-    "certain_union",
-    "compact",
-    "dense_weights",
-    "dequant_q4g32",
-    "down_projection",
-    "exact_mask",
-    "forward",
-    "forward_masked",
-    "gamma",
-    "guard_band_exact",
-    "guard_band_predictor",
-    "hot_mask",
-    "pre_activations",
-    "prob_band_exact",
-    "prob_band_predictor",
-    "PROB_LAMBDA",
-    "predictor_hidden",
-    "predictor_logits",
-    "predicted_mask",
-    "round_to_act",
-    "threshold_logit",
-    "union_mask",
-]

@@ -7,8 +7,8 @@ the FFN, the predictor, the mask or the down projection.  Both the CPU oracle
 are fed from here; neither side imports the other.
 """
 
-from .configs import CONFIGS, LayerConfig, config_by_name
-from .layers import (
+from .configs import CONFIGS, LayerConfig, config_by_name  # noqa: F401
+from .layers import (  # noqa: F401
     Layer,
     firing_probs,
     make_layer,
@@ -18,17 +18,3 @@ from .layers import (
     quantize_q4g32,
     pack_nibbles,
 )
-
-__all__ = [
-    "CONFIGS",
-    "LayerConfig",
-    "config_by_name",
-    "Layer",
-    "firing_probs",
-    "make_layer",
-    "make_tokens",
-    "make_lattice_layer",
-    "make_lattice_tokens",
-    "quantize_q4g32",
-    "pack_nibbles",
-]
