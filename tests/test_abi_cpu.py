@@ -183,3 +183,45 @@ def test_header_is_plain_c(tmp_path):
         r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I",
                             os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
         assert r.returncode == 0, f"{lang}: {r.stderr}"
+
+
+def test_c_caller_links_and_runs(tmp_path):
+    """A plain C99 program links libpi_ffn.so and calls it with no Python in between: the ABI
+    version, a workspace size equal to the one the binding reads, and host-side rejections with
+    their messages (no call here reaches a GPU)."""
+    import shutil
+    import subprocess
+    pi = _pi()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    expect = pi.workspace_bytes(pi.make_desc(4096, 11008, 1024, True, 1, "f16", "f16", "f16", 0.5))
+    src = tmp_path / "caller.c"
+    src.write_text(r'''#include <stdio.h>
+#include <string.h>
+#include "pi_ffn.h"
+
+int main(void) {
+  pi_ffn_desc d = {.d_model = 4096, .d_ffn = 11008, .rank = 1024, .gated = 1, .max_batch = 1,
+                   .w_dtype = PI_F16, .p_dtype = PI_F16, .act_dtype = PI_F16, .tau = 0.5f};
+  size_t bytes = 0;
+  if (pi_ffn_abi_version() != PI_FFN_ABI_VERSION) return 10;
+  if (pi_ffn_workspace_bytes(&d, &bytes) != PI_OK || bytes == 0) return 11;
+  printf("%zu\n", bytes);
+  d.d_model = 100;
+  if (pi_ffn_workspace_bytes(&d, &bytes) != PI_ERR_INVALID) return 12;
+  if (strstr(pi_last_error(), "d_model") == NULL) return 13;
+  if (pi_ffn_forward(NULL, NULL, 1, PI_MASK_DENSE, NULL, NULL, NULL, NULL) != PI_ERR_INVALID) return 14;
+  if (strstr(pi_last_error(), "handle") == NULL) return 15;
+  return 0;
+}
+''')
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(pi.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                        "-o", str(exe), f"-L{libdir}", "-lpi_ffn", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, (run.returncode, run.stderr)
+    assert int(run.stdout.strip()) == expect
